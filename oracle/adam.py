@@ -1,0 +1,181 @@
+"""One rank's mixed-precision Adam/AdamW step over its shard (oracle).
+
+What the pages fix: [Explainer, History, "The mixed-precision era"] and
+[Explainer, "The 16 Bytes per Parameter Audit"]: training keeps an fp16
+weight, an fp32 master copy and two fp32 Adam moments per parameter;
+[Explainer, Ch.02 "The Three Stages", "What each stage shards"]: under
+ZeRO-1/2 each rank updates only the optimizer states (and, with P_os+g, holds
+only the gradients) of its own partition, so the step below runs on one
+shard.  The pages give no update formula.  The steps are read as:
+
+  1. unscale the 16-bit gradient by the loss scale and detect inf/NaN
+     (dynamic loss scaling, Micikevicius et al. 2018);
+  2. squared L2 norm of the unscaled gradient, for max-norm clipping
+     (Pascanu et al. 2013, coefficient min(1, max_norm / (norm + 1e-6)));
+  3. Adam with bias correction (Kingma & Ba 2015, eps outside the square
+     root) and decoupled weight decay scaled by the learning rate
+     (Loshchilov & Hutter 2019 with the schedule multiplier equal to lr);
+  4. round the updated fp32 master weight to the 16-bit parameter copy.
+A step whose gradient holds any inf/NaN is skipped: no state changes, the step
+counter does not advance and the loss scale is reduced.
+
+Everything is float64; stored results are rounded once to float32 (master,
+momentum, variance) and from that float32 master to fp16/bf16 (parameter).
+"""
+from dataclasses import dataclass, replace
+from fractions import Fraction
+import math
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+
+from .formats import FORMATS, decode16, encode16_rne, is_nonfinite16
+
+_EXACT_CHUNK = 1 << 24
+
+
+def _sum_squares_exact(bits: np.ndarray, fmt: str) -> Fraction:
+    """Exact sum of squares of the finite 16-bit values, as a rational.
+
+    Each finite value is +-M * 2^E with integer significand M.  Its square is
+    M^2 * 2^(2E); summing the integers M^2 per exponent E is exact (every
+    partial sum is an integer below 2^53 for chunks of 2^24 elements), and the
+    per-exponent sums are combined in exact rational arithmetic.
+    """
+    ebits, mbits, bias = FORMATS[fmt]
+    emax_field = (1 << ebits) - 1
+    emin = 1 - bias
+    total = Fraction(0)
+    b_all = np.asarray(bits)
+    for s in range(0, b_all.size, _EXACT_CHUNK):
+        b = b_all[s:s + _EXACT_CHUNK].astype(np.int64) & 0xFFFF
+        e = (b >> mbits) & emax_field
+        f = b & ((1 << mbits) - 1)
+        finite = e != emax_field
+        e, f = e[finite], f[finite]
+        M = np.where(e == 0, f, f + (1 << mbits))
+        E = np.where(e == 0, emin - mbits, e - bias - mbits)   # value = M * 2^E
+        idx = E - (emin - mbits)                                # >= 0
+        per_exp = np.bincount(idx, weights=(M * M).astype(np.float64))
+        for i in np.nonzero(per_exp)[0]:
+            total += Fraction(int(per_exp[i])) * Fraction(2) ** (2 * (int(i) + emin - mbits))
+    return total
+
+
+def shard_sqnorm_overflow(grad_bits: np.ndarray, fmt: str, inv_loss_scale: float) -> Tuple[float, bool]:
+    """(sq, overflow) for one gradient shard.
+
+    overflow: some element is inf or NaN (tested on its exponent bits, never
+    inferred from the norm).  sq = sum_i (g_i * inv_loss_scale)^2 over the
+    whole shard (padding zeros included), computed exactly and rounded once
+    to float64; +inf if the shard holds an inf and no NaN, NaN if it holds a
+    NaN.
+    """
+    bits = np.asarray(grad_bits)
+    bad = is_nonfinite16(bits, fmt)
+    overflow = bool(bad.any())
+    if overflow:
+        vals = decode16(bits[bad], fmt)
+        return (math.nan if np.isnan(vals).any() else math.inf), True
+    exact = _sum_squares_exact(bits, fmt) * Fraction(inv_loss_scale) ** 2
+    return float(exact), False
+
+
+def global_sqnorm_overflow(shards: Iterable[np.ndarray], fmt: str,
+                           inv_loss_scale: float) -> Tuple[float, bool]:
+    """The data-parallel reduction of the per-rank results: the global sum of
+    squares over all shards (exact, one rounding) and the OR of the flags."""
+    total, overflow, has_nan = Fraction(0), False, False
+    for bits in shards:
+        bits = np.asarray(bits)
+        bad = is_nonfinite16(bits, fmt)
+        if bad.any():
+            overflow = True
+            has_nan |= bool(np.isnan(decode16(bits[bad], fmt)).any())
+        else:
+            total += _sum_squares_exact(bits, fmt)
+    if overflow:
+        return (math.nan if has_nan else math.inf), True
+    return float(total * Fraction(inv_loss_scale) ** 2), False
+
+
+def clip_coefficient(sq: float, max_grad_norm: float) -> float:
+    """Max-norm clipping coefficient from the global squared norm:
+    min(1, max_norm / (norm + 1e-6)); 1 when clipping is off (max_norm <= 0)."""
+    if max_grad_norm <= 0.0:
+        return 1.0
+    norm = math.sqrt(sq)
+    return min(1.0, max_grad_norm / (norm + 1e-6))
+
+
+def grad_scale(inv_loss_scale: float, coef: float) -> float:
+    """Factor applied to the raw 16-bit gradient: unscale, then clip."""
+    return inv_loss_scale * coef
+
+
+def adam_update(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
+                grad_bits: np.ndarray, grad_fmt: str, gscale: float, *, lr: float,
+                beta1: float, beta2: float, eps: float, weight_decay: float, step: int,
+                param_fmt: Optional[str] = None):
+    """Bias-corrected Adam with decoupled weight decay, elementwise, float64.
+
+    step is the 1-based index t of the step being applied.  Returns float32
+    (master, exp_avg, exp_avg_sq) and the uint16 bits of the 16-bit parameter
+    copy rounded from the new float32 master (None if param_fmt is None).
+    """
+    if step < 1:
+        raise ValueError("step must be >= 1")
+    p = np.asarray(master, dtype=np.float64)
+    m = np.asarray(exp_avg, dtype=np.float64)
+    v = np.asarray(exp_avg_sq, dtype=np.float64)
+    g = decode16(grad_bits, grad_fmt) * gscale
+    m_new = beta1 * m + (1.0 - beta1) * g
+    v_new = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m_new / (1.0 - beta1 ** step)
+    v_hat = v_new / (1.0 - beta2 ** step)
+    p_new = p - lr * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * p)
+    master32 = p_new.astype(np.float32)
+    param = encode16_rne(master32, param_fmt) if param_fmt is not None else None
+    return master32, m_new.astype(np.float32), v_new.astype(np.float32), param
+
+
+@dataclass(frozen=True)
+class LossScalerState:
+    """Dynamic loss scale.  On an overflowing step: skip it, multiply the
+    scale by `backoff` (floored at `min_scale`) and reset the clean-step count.
+    After `growth_interval` clean steps in a row: multiply the scale by
+    `growth` and reset the count.  backoff = growth = 1 gives a static scale."""
+    scale: float
+    good_steps: int = 0
+    min_scale: float = 1.0
+    backoff: float = 0.5
+    growth: float = 2.0
+    growth_interval: int = 1000
+
+
+def loss_scaler_update(s: LossScalerState, overflow: bool) -> Tuple[LossScalerState, bool]:
+    """Return (new state, skip)."""
+    if overflow:
+        return replace(s, scale=max(s.scale * s.backoff, s.min_scale), good_steps=0), True
+    good = s.good_steps + 1
+    if good >= s.growth_interval:
+        return replace(s, scale=s.scale * s.growth, good_steps=0), False
+    return replace(s, good_steps=good), False
+
+
+def shard_step(master, exp_avg, exp_avg_sq, grad_bits, grad_fmt, param_fmt, *, global_sq,
+               global_overflow, inv_loss_scale, max_grad_norm, lr, beta1, beta2, eps,
+               weight_decay, step):
+    """Steps 2-4 on one shard given the data-parallel-reduced (sq, overflow).
+
+    Returns (master, exp_avg, exp_avg_sq, param_bits_or_None, applied).  On
+    overflow nothing is computed: the inputs come back unchanged, no parameter
+    is written and applied is False.
+    """
+    if global_overflow:
+        return master, exp_avg, exp_avg_sq, None, False
+    coef = clip_coefficient(global_sq, max_grad_norm)
+    out = adam_update(master, exp_avg, exp_avg_sq, grad_bits, grad_fmt,
+                      grad_scale(inv_loss_scale, coef), lr=lr, beta1=beta1, beta2=beta2,
+                      eps=eps, weight_decay=weight_decay, step=step, param_fmt=param_fmt)
+    return (*out, True)
