@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark: one ZeRO rank's partitioned mixed-precision AdamW shard step on
+one MI355X.
+
+A step is the whole hot path on this rank's shard, through the C ABI:
+  unscale + inf/NaN detection + squared norm (two kernels), the fused AdamW
+  update with clipping and 16-bit parameter writeback (one kernel), then the
+  4-byte overflow flag read back for the loss-scale / step-counter update.
+Inputs are seeded synthetic values uploaded to HBM before timing.
+
+Prints one JSON line.  `value` is params/s of the whole step; `roofline`
+reports the fused AdamW kernel (the dominant one) against MI355X's 8 TB/s HBM
+peak, from HIP events recorded on the stream it runs on.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E, published
+ADAM_BYTES_PER_PARAM = 28           # 2 grad + 3x4 read + 3x4 write + 2 param
+NORM_BYTES_PER_PARAM = 2            # gradient read once
+STEP_BYTES_PER_PARAM = ADAM_BYTES_PER_PARAM + NORM_BYTES_PER_PARAM
+METRIC = "shard optimizer-step params/sec and achieved HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_partition_amd", "csrc", "shard_step.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on a different kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get("adam_update", {}).get(workload)
+    if not rec or rec.get("kernel_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def upload_inputs(w, begin, S, grad_dtype, block_chunks=16):
+    """Generate the shard's seeded inputs block by block and copy them to HBM."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    dev = "cuda"
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[grad_dtype]
+    P = torch.empty(S, dtype=torch.float32, device=dev)
+    M = torch.empty(S, dtype=torch.float32, device=dev)
+    V = torch.empty(S, dtype=torch.float32, device=dev)
+    G = torch.empty(S, dtype=tdt, device=dev)
+    blk = block_chunks * W.CHUNK
+    for lo in range(0, S, blk):
+        cnt = min(blk, S - lo)
+        for name, dst in (("master", P), ("exp_avg", M), ("exp_avg_sq", V)):
+            dst[lo:lo + cnt].copy_(torch.from_numpy(W.fill(w, name, begin + lo, cnt)))
+        g = W.fill(w, "grad", begin + lo, cnt, step=w.step)
+        G[lo:lo + cnt].copy_(torch.from_numpy(g.view(np.int16)).view(tdt))
+        print(f"# uploaded {lo + cnt}/{S} elements", file=sys.stderr, flush=True)
+    return P, M, V, G
+
+
+def cpu_baseline(w, begin, S, target_s=12.0):
+    """The CPU oracle's full step (norm + AdamW) on a bounded contiguous
+    sample of the same shard, single process."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    import workloads as W
+
+    def run(n):
+        p, m, v, g = W.shard_inputs(w, begin, n)
+        t0 = time.perf_counter()
+        inv = 1.0 / w.loss_scale
+        sq, ovf = oracle.shard_sqnorm_overflow(g, w.grad_dtype, inv)
+        oracle.shard_step(p, m, v, g, w.grad_dtype, w.param_dtype, global_sq=sq, global_overflow=ovf,
+                          inv_loss_scale=inv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
+                          beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.step)
+        return time.perf_counter() - t0
+
+    n0 = min(S, 1 << 18)
+    run(n0)                                    # warm the allocator
+    t = run(n0)
+    n = int(min(S, max(n0, n0 * target_s / max(t, 1e-9))))
+    n = min(n, 1 << 26)
+    t = run(n)
+    return {"value": n / t, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} params of the same shard, one step (exact norm + AdamW, float64 NumPy), "
+                      f"single process, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt1t",
+                    help="tiny | gpt2 | llama7b | gpt100b | gpt1t (default: one rank's shard of a 1T model)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's shard step on ONE GPU; --gpus {args.gpus} is not supported "
+              "(the data-parallel collectives around the step are not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import workloads as W
+    w = W.get(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is touched (the oracle is host-only)
+        import zero_sharded_mixed_partition_amd as Z
+        _, S0, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+        cpu = cpu_baseline(w, w.rank * S0, S0)
+        print(f"# cpu baseline {cpu['value']:.4g} params/s", file=sys.stderr, flush=True)
+
+    import torch
+
+    import zero_sharded_mixed_partition_amd as Z
+    torch.cuda.set_device(0)
+    offsets, S, padded = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+    begin = w.rank * S
+    print(f"# workload {w.name}: shard {S} params at flat offset {begin}", file=sys.stderr, flush=True)
+    P, M, V, G = upload_inputs(w, begin, S, w.grad_dtype)
+    pdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.param_dtype]
+    par = torch.empty(S, dtype=pdt, device="cuda")
+    opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                      max_grad_norm=w.max_grad_norm,
+                      scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
+                      applied_steps=w.step - 1)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        opt.unscale_norm(G)
+        if ev is not None:
+            ev[1].record()
+        opt.apply(G, par)
+        if ev is not None:
+            ev[2].record()
+        return opt.finish()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    skipped = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        skipped += step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    norm_ms = sorted(a.elapsed_time(b) for a, b, _ in evs)
+    adam_ms = sorted(b.elapsed_time(c) for _, b, c in evs)
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
+    adam_avg = mean(adam_ms)
+    adam_gbps = ADAM_BYTES_PER_PARAM * S / (adam_avg * 1e-3) / 1e9
+    step_gbps = STEP_BYTES_PER_PARAM * S / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+
+    # practical ceiling: torch's device copy over the same 14 B/param read + 14 B/param write
+    src = torch.empty(S * 14 // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del src, dst
+
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shard_params": S, "n_d": w.n_d, "rank": w.rank,
+                   "flat_offset": begin, "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
+                   "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
+                   "weight_decay": w.weight_decay, "param_layout": w.param_layout,
+                   "algorithmic_bytes_per_param": STEP_BYTES_PER_PARAM},
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": ADAM_BYTES_PER_PARAM * S, "avg_ms": adam_avg,
+                     "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9)},
+        "norm_pass": {"avg_ms": mean(norm_ms), "gbps": NORM_BYTES_PER_PARAM * S / (mean(norm_ms) * 1e-3) / 1e9},
+        "copy_ceiling_gbps": copy_gbps,
+        "skipped_steps": skipped,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * zero_shard.h -- C ABI of one ZeRO data-parallel rank's partitioned
+ * mixed-precision Adam step (P_os+g), for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what is computed:
+ *  - ZeRO method entry (Sharded Data Parallel Methods catalogue),
+ *    description: model states are partitioned across the data-parallel
+ *    processes instead of replicated.
+ *  - Explainer "Data Parallelism Without the Copies" of the paper "ZeRO:
+ *    Memory Optimizations Toward Training Trillion Parameter Models":
+ *    section "The 16 Bytes per Parameter Audit" (fp16 weight, fp32 master,
+ *    two fp32 Adam moments per parameter); Ch.02 "The Three Stages" (what
+ *    P_os, P_os+g and P_os+g+p shard); Ch.05 "Super-Linear Scaling" (stage
+ *    table).
+ *  The pages give no update formula.  The steps implemented are dynamic loss
+ *  scaling with inf/NaN skip (Micikevicius et al. 2018), global max-norm
+ *  clipping (Pascanu et al. 2013; coefficient min(1, max/(norm + 1e-6))),
+ *  bias-corrected Adam (Kingma & Ba 2015, eps outside the square root) with
+ *  decoupled weight decay scaled by the learning rate (Loshchilov & Hutter
+ *  2019), and round-to-nearest-even writeback of the 16-bit parameter copy.
+ *
+ * Conventions for every function:
+ *  - Returns an int status: ZERO_OK (0) or a negative zero_status.  Nothing
+ *    throws.  On error a detail string is available from zero_last_error()
+ *    (thread-local, valid until the next call on the same thread).
+ *  - An invalid argument is detected on the host before anything is
+ *    enqueued: on error no device work has been queued.
+ *  - Device functions only enqueue work on `hip_stream` (a hipStream_t; NULL
+ *    is the default stream) and return; results are valid once the stream
+ *    has reached that point.  They never synchronize and never allocate.
+ *  - The caller owns every host array and device buffer.  Device pointers
+ *    must point to device memory of the current HIP device and be 16-byte
+ *    aligned (ZERO_EALIGN otherwise).  The library keeps no state apart from
+ *    the thread-local error string.
+ *  - Sizes are element counts in int64; n = 0 is a valid no-op.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_SHARD_ABI_VERSION 1
+
+typedef enum {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1,   /* bad argument (null pointer, n < 0, unknown dtype, ...) */
+    ZERO_EALIGN = -2,   /* device pointer not 16-byte aligned */
+    ZERO_ERANGE = -3,   /* a size overflows int64 or a kernel limit */
+    ZERO_ENOSPC = -4,   /* caller's output array or workspace too small */
+    ZERO_EHIP = -5      /* HIP runtime reported an error at launch */
+} zero_status;
+
+/* 16-bit floating-point formats of the gradient and of the parameter copy. */
+enum { ZERO_F16 = 1, ZERO_BF16 = 2 };
+
+/* Returns ZERO_SHARD_ABI_VERSION of the built library. */
+int zero_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Partition plan (host only, integer arithmetic).
+ *
+ * ZeRO method entry, description; explainer, History ("ZeRO":
+ * partition-and-all-gather) and "The 16 Bytes per Parameter Audit": every
+ * rank owns one partition of the flattened model state.  Layout: tensors end
+ * to end in list order with no gaps, the flat buffer padded at its end to
+ * padded_total = n_d * S where S = align * ceil(T / (n_d * align)) and T is
+ * the total element count; rank r owns flat range [r*S, (r+1)*S).
+ *
+ *  dims      all tensors' dimensions concatenated (int64, each >= 0);
+ *            may be NULL if the sum of ndims is 0
+ *  ndims     ndims[i] = number of dimensions of tensor i (0 = scalar, one
+ *            element); NULL allowed only if n_tensors == 0
+ *  n_tensors >= 0
+ *  n_d       data-parallel degree, >= 1
+ *  align     partition size granularity in elements, >= 1
+ *  tensor_offsets  out, [n_tensors] flat start of each tensor (may be NULL
+ *            if n_tensors == 0)
+ *  partition_numel out, S;  padded_total  out, n_d * S
+ * Errors: ZERO_EINVAL (null/negative), ZERO_ERANGE (int64 overflow).
+ * ------------------------------------------------------------------------- */
+int zero_partition_plan(const int64_t* dims, const int32_t* ndims, int32_t n_tensors,
+                        int32_t n_d, int64_t align, int64_t* tensor_offsets,
+                        int64_t* partition_numel, int64_t* padded_total);
+
+/* One nonempty intersection of a tensor with a rank's partition: elements
+ * [tensor_begin, tensor_begin + numel) of tensor `tensor` (row-major flat
+ * index) sit at [shard_begin, shard_begin + numel) of the rank's shard. */
+typedef struct {
+    int32_t tensor;
+    int32_t reserved;       /* 0 */
+    int64_t tensor_begin;
+    int64_t shard_begin;
+    int64_t numel;
+} zero_fragment;
+
+/* Fragments of rank `rank` in list order.  Writes min(count, capacity)
+ * entries to `out` (may be NULL when capacity == 0) and the required count
+ * to *count; returns ZERO_ENOSPC if capacity < required (then *count still
+ * holds the required count).  Other arguments as zero_partition_plan. */
+int zero_rank_fragments(const int64_t* dims, const int32_t* ndims, int32_t n_tensors,
+                        int32_t n_d, int64_t align, int32_t rank, zero_fragment* out,
+                        int32_t capacity, int32_t* count);
+
+/* ---------------------------------------------------------------------------
+ * Step 1+2: unscale, inf/NaN detection, squared L2 norm of one gradient shard.
+ *
+ *  grad        device, [n] 16-bit values of format grad_dtype (raw bits)
+ *  inv_loss_scale  1 / loss scale (> 0, finite)
+ *  d_sqnorm    device, out: one double = sum_i (grad_i * inv_loss_scale)^2
+ *              (+inf if the shard holds an inf and no NaN, NaN if it holds
+ *              a NaN).  Each square is exact in float64; the sum is taken
+ *              in float64 in a fixed order that depends only on n, so the
+ *              result is bit-identical from run to run.
+ *  d_overflow  device, out: one int32, 1 if any element is +-inf or NaN
+ *              (tested on the exponent bits, never inferred from the norm),
+ *              else 0
+ *  d_workspace device scratch of at least zero_norm_workspace_bytes(n)
+ *              bytes (no initial contents needed; clobbered)
+ * The grad shard is only read.  Two kernels are enqueued (block partials,
+ * then a one-block fixed-order combine).  For n == 0 the outputs are
+ * written as 0 by one small kernel.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOSPC (workspace), ZERO_ERANGE,
+ * ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+size_t zero_norm_workspace_bytes(int64_t n);
+
+int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64_t n,
+                                     double inv_loss_scale, double* d_sqnorm,
+                                     int32_t* d_overflow, void* d_workspace,
+                                     size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps 3+4: fused Adam/AdamW update of one shard and 16-bit writeback.
+ *
+ * Hyperparameters are double; the host derives the per-step float32
+ * coefficients from them in double and rounds each once.  `step` is the
+ * 1-based index t of the step being applied (bias corrections 1 - beta^t).
+ * max_grad_norm <= 0 disables clipping.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+    double inv_loss_scale, max_grad_norm;
+} zero_adam_params;
+
+/*  master, exp_avg, exp_avg_sq  device, [n] float32, updated in place
+ *  grad        device, [n] 16-bit gradient (grad_dtype), read only
+ *  param_out   device, [n] 16-bit parameter copy (param_dtype) written as
+ *              round-to-nearest-even of the new float32 master; NULL skips
+ *              the writeback.  For the ZeRO-2 layout pass the rank's slice
+ *              (offset r*S) of the full flat parameter buffer; for ZeRO-3 a
+ *              shard-local buffer.
+ *  d_global_sqnorm  device double: the data-parallel sum of every rank's
+ *              d_sqnorm; read by the kernel to form the clip coefficient
+ *              min(1, max/(sqrt(sq) + 1e-6)) in double.  May be NULL only
+ *              when clipping is disabled.
+ *  d_global_overflow  device int32: the OR of every rank's d_overflow.  If
+ *              nonzero when the kernel runs, the kernel writes nothing at all
+ *              (skipped step).  NULL: never skip.
+ * Per element (float32): g = grad * gscale with gscale = float(inv_scale *
+ * coef); m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g^2;
+ * p = p*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps).
+ * Streams 28 bytes per element (2 grad + 3x4 read, 3x4 write + 2 param).
+ * grad must not alias master, exp_avg, exp_avg_sq or param_out.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                         int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                         const zero_adam_params* hp, const double* d_global_sqnorm,
+                         const int32_t* d_global_overflow, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Step 2 (scalar, host): dynamic loss scale update after a step.
+ * On overflow: *skip_out = 1, scale = max(scale*backoff, min_scale),
+ * good_steps = 0.  Otherwise *skip_out = 0, good_steps += 1 and, when it
+ * reaches growth_interval, scale *= growth and good_steps = 0.
+ * backoff = growth = 1 gives a static scale.  The caller advances its step
+ * counter t only when *skip_out == 0.
+ * Errors: ZERO_EINVAL (null, scale <= 0, min_scale <= 0, backoff or growth
+ * <= 0, growth_interval < 1).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    double scale, min_scale, backoff, growth;
+    int64_t growth_interval, good_steps;
+} zero_loss_scaler;
+
+int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out);
+
+/* Static description of a status code, and the thread-local detail of the
+ * last failing call (empty string if none). */
+const char* zero_status_string(int status);
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZERO_SHARD_H */

@@ -1,0 +1,90 @@
+"""Shared helpers for the GPU parity tests: device upload/download of seeded
+inputs and the tolerance checks, written out once.
+
+Tolerances (the bar every GPU result must meet against the oracle):
+  plan, overflow flags, skip decisions   bit-exact
+  fp32 master / exp_avg / exp_avg_sq     |x - ref| <= max(1e-5 * |ref|, 1e-7)
+  gradient norm                          |n - ref| <= 1e-5 * ref
+  fp16 / bf16 parameter copy             at most 1 ulp apart (distance of the
+                                         16-bit patterns on the ordered integer
+                                         line, +0 and -0 equal)
+Besides the bar, `strict_*` checks bound the float32 arithmetic more tightly
+(a mis-rounded coefficient such as 1 - beta2 formed in float32 passes the bar
+on tiny values but not these).
+"""
+import numpy as np
+
+REL, ABS = 1e-5, 1e-7
+
+
+def to_device(a: np.ndarray, fmt: str = None):
+    import torch
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16).copy()).cuda()
+        return t.view({"f16": torch.float16, "bf16": torch.bfloat16}[fmt])
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bits_of(t) -> np.ndarray:
+    """Raw uint16 bits of a 16-bit device tensor."""
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_f32(name, got, ref, rel=REL, abs_=ABS):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, name
+    err = np.abs(got - ref)
+    tol = np.maximum(rel * np.abs(ref), abs_)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} out of tolerance; e.g. idx {i.tolist()} "
+                             f"got {got[i].tolist()} ref {ref[i].tolist()}")
+    return float(np.max(err / np.maximum(np.abs(ref), 1e-30))) if err.size else 0.0
+
+
+def ordered16(bits: np.ndarray) -> np.ndarray:
+    """Map 16-bit float patterns to integers ordered like the values
+    (+0 and -0 both map to 0)."""
+    b = bits.astype(np.int64) & 0xFFFF
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def check_param(name, got_bits, ref_bits, max_ulp=1):
+    d = np.abs(ordered16(got_bits) - ordered16(ref_bits))
+    bad = d > max_ulp
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{name}: {bad.sum()} params more than {max_ulp} ulp off; idx {i.tolist()} "
+                             f"got {got_bits[i].tolist()} ref {ref_bits[i].tolist()}")
+    return int(d.max()) if d.size else 0
+
+
+def check_norm(got_sq: float, ref_sq: float, rel=1e-5):
+    if np.isnan(ref_sq) or np.isinf(ref_sq):
+        assert (np.isnan(got_sq) and np.isnan(ref_sq)) or got_sq == ref_sq, (got_sq, ref_sq)
+        return
+    n, r = np.sqrt(got_sq), np.sqrt(ref_sq)
+    assert abs(n - r) <= rel * r, f"norm {n!r} vs oracle {r!r}"
+
+
+def strict_v(got, ref):
+    """Second moment: both terms are nonnegative, so float32 keeps a few ulp
+    relative error everywhere."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    assert (err <= 1e-6 * np.abs(ref) + 1e-40).all(), float(np.max(err / np.maximum(ref, 1e-38)))
+
+
+def compare_step(got, ref, what=""):
+    """got/ref: (master, exp_avg, exp_avg_sq, param_bits or None)."""
+    out = {}
+    for k, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+        out[name] = check_f32(f"{what}{name}", got[k], ref[k])
+    strict_v(got[2], ref[2])
+    if ref[3] is not None:
+        out["param_ulp"] = check_param(f"{what}param", got[3], ref[3])
+    return out

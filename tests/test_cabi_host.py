@@ -1,0 +1,162 @@
+"""Host-side tests of the C-ABI library (no GPU): it loads, exports every
+function include/*.h declares, and its host logic (partition plan, rank
+fragments, loss scaler, argument validation) agrees bit-exactly with the
+oracle.  No device compute entry point is executed with valid arguments here;
+the device entry points are only called with arguments the host validation
+rejects before anything is enqueued."""
+import ctypes
+import glob
+import os
+import random
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import workloads as W
+import zero_sharded_mixed_partition_amd as Z
+from zero_sharded_mixed_partition_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(zero_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert len(declared) >= 9
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(L.SIGNATURES), "binding signatures out of sync with the header"
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (zero_\w+)", out))
+    assert declared <= exported
+
+
+def test_abi_version():
+    assert Z.zero_abi_version() == 1
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_matches_oracle_random(seed):
+    rng = random.Random(seed)
+    shapes = [tuple(rng.randint(0, 50) for _ in range(rng.randint(0, 3))) for _ in range(rng.randint(0, 12))]
+    for n_d in (1, 2, 3, 8, 13):
+        for align in (1, 4, 128):
+            assert Z.zero_partition_plan(shapes, n_d, align) == oracle.partition_plan(shapes, n_d, align)
+            for r in range(n_d):
+                assert Z.zero_rank_fragments(shapes, n_d, align, r) == oracle.rank_fragments(shapes, n_d, align, r)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_plan_matches_oracle_workloads(name):
+    w = W.get(name)
+    assert Z.zero_partition_plan(w.shapes, w.n_d, w.align) == oracle.partition_plan(w.shapes, w.n_d, w.align)
+    for r in sorted({0, w.rank, w.n_d - 1}):
+        assert Z.zero_rank_fragments(w.shapes, w.n_d, w.align, r) == oracle.rank_fragments(w.shapes, w.n_d, w.align, r)
+
+
+def test_plan_errors():
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(4,)], 0, 1)
+    assert e.value.status == L.ZERO_EINVAL
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(4,)], 1, 0)
+    assert e.value.status == L.ZERO_EINVAL
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(-1, 3)], 2, 1)
+    assert e.value.status == L.ZERO_EINVAL
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(1 << 40, 1 << 40)], 2, 1)
+    assert e.value.status == L.ZERO_ERANGE
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(1 << 62,), (1 << 62,)], 1, 1)
+    assert e.value.status == L.ZERO_ERANGE
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_partition_plan([(8,)], 1 << 30, 1 << 40)
+    assert e.value.status == L.ZERO_ERANGE
+    with pytest.raises(Z.ZeroShardError) as e:
+        Z.zero_rank_fragments([(8,)], 2, 1, 2)
+    assert e.value.status == L.ZERO_EINVAL
+
+
+def test_fragments_enospc_reports_count():
+    dims = (ctypes.c_int64 * 3)(10, 10, 10)
+    ndims = (ctypes.c_int32 * 3)(1, 1, 1)
+    count = ctypes.c_int32()
+    buf = (L.zero_fragment * 1)()
+    st = L.lib().zero_rank_fragments(dims, ndims, 3, 1, 1, 0, buf, 1, ctypes.byref(count))
+    assert st == L.ZERO_ENOSPC and count.value == 3 and buf[0].numel == 10
+
+
+def test_edge_plans():
+    assert Z.zero_partition_plan([], 4, 128) == ([], 0, 0)
+    assert Z.zero_rank_fragments([], 4, 128, 3) == []
+    assert Z.zero_partition_plan([()], 3, 1) == ([0], 1, 3)
+    assert Z.zero_rank_fragments([()], 3, 1, 2) == []
+
+
+def test_loss_scaler_matches_oracle():
+    rng = random.Random(5)
+    ours = Z.LossScaler(scale=65536.0, growth_interval=7)
+    ref = oracle.LossScalerState(scale=65536.0, growth_interval=7)
+    for _ in range(500):
+        ovf = rng.random() < 0.1
+        skip = Z.zero_loss_scaler_update(ours, ovf)
+        ref, rskip = oracle.loss_scaler_update(ref, ovf)
+        assert skip == rskip and ours.scale == ref.scale and ours.good_steps == ref.good_steps
+
+
+def test_loss_scaler_invalid():
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_loss_scaler_update(Z.LossScaler(scale=0.0), False)
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_loss_scaler_update(Z.LossScaler(growth_interval=0), False)
+
+
+def test_device_entry_points_reject_bad_arguments_on_host():
+    """Arguments the host-side validation rejects: nothing reaches the GPU."""
+    lib = L.lib()
+    hp = L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 0.0)
+    buf = ctypes.create_string_buffer(64)
+    aligned = (ctypes.addressof(buf) + 15) & ~15
+    # bad dtype / negative n / null pointers / bad hyperparameters / misalignment
+    assert lib.zero_shard_unscale_norm_overflow(aligned, 3, 8, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
+    assert lib.zero_shard_unscale_norm_overflow(aligned, 1, -1, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
+    assert lib.zero_shard_unscale_norm_overflow(aligned, 1, 8, 0.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
+    assert lib.zero_shard_unscale_norm_overflow(aligned + 2, 1, 8, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EALIGN
+    assert lib.zero_shard_unscale_norm_overflow(aligned, 1, 8, 1.0, aligned, aligned, aligned, 0, None) == L.ZERO_ENOSPC
+    A = ctypes.byref(hp)
+    assert lib.zero_shard_adam_step(None, None, None, None, 1, None, 0, 8, A, None, None, None) == L.ZERO_EINVAL
+    assert lib.zero_shard_adam_step(aligned, aligned, aligned, aligned, 7, None, 0, 8, A, None, None, None) == L.ZERO_EINVAL
+    bad = [L.zero_adam_params(1e-3, 1.0, 0.999, 1e-8, 0.0, 1, 1.0, 0.0),
+           L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 0, 1.0, 0.0),
+           L.zero_adam_params(-1.0, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 0.0),
+           L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0.0, 0.0),
+           L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 1.0)]   # clip without d_global_sqnorm
+    for b in bad:
+        assert lib.zero_shard_adam_step(aligned, aligned + 16, aligned + 32, aligned + 48, 1, None, 0, 4,
+                                        ctypes.byref(b), None, None, None) == L.ZERO_EINVAL
+    assert lib.zero_shard_adam_step(aligned + 4, aligned + 16, aligned + 32, aligned + 48, 1, None, 0, 4, A,
+                                    None, None, None) == L.ZERO_EALIGN
+    # grad aliasing master
+    assert lib.zero_shard_adam_step(aligned, aligned + 16, aligned + 32, aligned, 1, None, 0, 4, A,
+                                    None, None, None) == L.ZERO_EINVAL
+    # n == 0 is a no-op that needs no pointers
+    assert lib.zero_shard_adam_step(None, None, None, None, 1, None, 0, 0, A, None, None, None) == L.ZERO_OK
+    assert L.lib().zero_last_error() == b""
+
+
+def test_workspace_size():
+    assert Z.zero_norm_workspace_bytes(0) >= 12
+    assert Z.zero_norm_workspace_bytes(-1) == 0
+    assert Z.zero_norm_workspace_bytes(1 << 40) <= 2048 * 12 + 256
+    assert Z.zero_norm_workspace_bytes(10**6) % 256 == 0

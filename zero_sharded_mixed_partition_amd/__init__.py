@@ -1,0 +1,176 @@
+"""One ZeRO data-parallel rank's partitioned mixed-precision Adam step on
+AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/zero_shard.h (libzero_shard.so,
+hand-written HIP kernels).  The functions keep the C names and only marshal
+arguments: torch tensors supply device memory (their data pointers) and
+torch's current HIP stream supplies the stream; every step of the update runs
+in the library's kernels.
+
+    zero_partition_plan(shapes, n_d, align) -> (offsets, S, padded_total)
+    zero_rank_fragments(shapes, n_d, align, rank) -> [(tensor, tensor_begin, shard_begin, numel)]
+    zero_norm_workspace_bytes(n) -> int
+    zero_shard_unscale_norm_overflow(grad, inv_loss_scale, sqnorm, overflow, workspace)
+    zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp, global_sqnorm, global_overflow)
+    zero_loss_scaler_update(scaler, overflow) -> skip
+"""
+import ctypes
+from typing import List, Optional, Sequence, Tuple
+
+from . import _lib as _L
+from ._lib import (ZERO_BF16, ZERO_F16, ZeroShardError, zero_adam_params,  # noqa: F401
+                   zero_fragment, zero_loss_scaler)
+
+__all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_bytes",
+           "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_loss_scaler_update",
+           "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZeroShardError", "AdamHyper",
+           "LossScaler", "dtype_code", "ShardAdam"]
+
+
+def zero_abi_version() -> int:
+    return int(_L.lib().zero_abi_version())
+
+
+def _shape_arrays(shapes: Sequence[Sequence[int]]):
+    n = len(shapes)
+    flat = [int(d) for s in shapes for d in s]
+    dims = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+    ndims = (ctypes.c_int32 * max(1, n))(*[len(s) for s in shapes])
+    return dims, ndims, n
+
+
+def zero_partition_plan(shapes: Sequence[Sequence[int]], n_d: int, align: int) -> Tuple[List[int], int, int]:
+    dims, ndims, n = _shape_arrays(shapes)
+    offs = (ctypes.c_int64 * max(1, n))()
+    S, padded = ctypes.c_int64(), ctypes.c_int64()
+    _L.check(_L.lib().zero_partition_plan(dims, ndims, n, n_d, align, offs, ctypes.byref(S),
+                                          ctypes.byref(padded)), "zero_partition_plan")
+    return list(offs[:n]), S.value, padded.value
+
+
+def zero_rank_fragments(shapes: Sequence[Sequence[int]], n_d: int, align: int,
+                        rank: int) -> List[Tuple[int, int, int, int]]:
+    dims, ndims, n = _shape_arrays(shapes)
+    count = ctypes.c_int32()
+    st = _L.lib().zero_rank_fragments(dims, ndims, n, n_d, align, rank, None, 0, ctypes.byref(count))
+    if st not in (_L.ZERO_OK, _L.ZERO_ENOSPC):
+        _L.check(st, "zero_rank_fragments")
+    buf = (zero_fragment * max(1, count.value))()
+    _L.check(_L.lib().zero_rank_fragments(dims, ndims, n, n_d, align, rank, buf, count.value,
+                                          ctypes.byref(count)), "zero_rank_fragments")
+    return [(f.tensor, f.tensor_begin, f.shard_begin, f.numel) for f in buf[:count.value]]
+
+
+def zero_norm_workspace_bytes(n: int) -> int:
+    return int(_L.lib().zero_norm_workspace_bytes(n))
+
+
+def dtype_code(t) -> int:
+    """ZERO_F16 / ZERO_BF16 from a torch dtype (or pass the code through)."""
+    if isinstance(t, int):
+        return t
+    import torch
+    dt = t.dtype if hasattr(t, "dtype") else t
+    if dt == torch.float16:
+        return ZERO_F16
+    if dt == torch.bfloat16:
+        return ZERO_BF16
+    raise ValueError(f"unsupported 16-bit dtype {dt}")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def zero_shard_unscale_norm_overflow(grad, inv_loss_scale: float, sqnorm, overflow, workspace,
+                                     grad_dtype: Optional[int] = None, n: Optional[int] = None,
+                                     stream=None) -> None:
+    """Enqueue steps 1-2 on the current stream.  grad: float16/bfloat16 device
+    tensor (or raw pointer with grad_dtype and n); sqnorm: float64 [1];
+    overflow: int32 [1]; workspace: device tensor of at least
+    zero_norm_workspace_bytes(n) bytes."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = grad.numel() if n is None else n
+    wbytes = workspace.numel() * workspace.element_size()
+    _L.check(_L.lib().zero_shard_unscale_norm_overflow(_ptr(grad), gd, n, float(inv_loss_scale), _ptr(sqnorm),
+                                                       _ptr(overflow), _ptr(workspace), wbytes, _stream(stream)),
+             "zero_shard_unscale_norm_overflow")
+
+
+class AdamHyper:
+    """Adam/AdamW hyperparameters of one step (all double at the ABI)."""
+
+    def __init__(self, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1,
+                 inv_loss_scale=1.0, max_grad_norm=0.0):
+        self.lr, self.beta1, self.beta2, self.eps = lr, beta1, beta2, eps
+        self.weight_decay, self.step = weight_decay, step
+        self.inv_loss_scale, self.max_grad_norm = inv_loss_scale, max_grad_norm
+
+    def c(self) -> zero_adam_params:
+        return zero_adam_params(float(self.lr), float(self.beta1), float(self.beta2), float(self.eps),
+                                float(self.weight_decay), int(self.step), float(self.inv_loss_scale),
+                                float(self.max_grad_norm))
+
+
+def zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: AdamHyper, global_sqnorm=None,
+                         global_overflow=None, grad_dtype: Optional[int] = None,
+                         param_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """Enqueue steps 3-4 on the current stream (see include/zero_shard.h)."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
+    n = master.numel() if n is None else n
+    if not isinstance(master, int):
+        for t in (exp_avg, exp_avg_sq, grad) + (() if param_out is None else (param_out,)):
+            if t.numel() != n:
+                raise ValueError("shard tensors differ in length")
+    params = hp.c()
+    _L.check(_L.lib().zero_shard_adam_step(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
+                                           _ptr(param_out), pd, n, ctypes.byref(params), _ptr(global_sqnorm),
+                                           _ptr(global_overflow), _stream(stream)),
+             "zero_shard_adam_step")
+
+
+class LossScaler:
+    """Host-side dynamic loss scale (C struct zero_loss_scaler)."""
+
+    def __init__(self, scale=65536.0, min_scale=1.0, backoff=0.5, growth=2.0, growth_interval=1000,
+                 good_steps=0):
+        self.s = zero_loss_scaler(float(scale), float(min_scale), float(backoff), float(growth),
+                                  int(growth_interval), int(good_steps))
+
+    @property
+    def scale(self) -> float:
+        return self.s.scale
+
+    @property
+    def good_steps(self) -> int:
+        return self.s.good_steps
+
+    @classmethod
+    def static(cls, scale=1.0):
+        return cls(scale=scale, min_scale=scale, backoff=1.0, growth=1.0)
+
+
+def zero_loss_scaler_update(scaler: LossScaler, overflow: bool) -> bool:
+    skip = ctypes.c_int32()
+    _L.check(_L.lib().zero_loss_scaler_update(ctypes.byref(scaler.s), 1 if overflow else 0, ctypes.byref(skip)),
+             "zero_loss_scaler_update")
+    return bool(skip.value)
+
+
+from .shard import ShardAdam  # noqa: E402

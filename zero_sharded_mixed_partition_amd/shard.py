@@ -1,0 +1,72 @@
+"""ShardAdam: one rank's optimizer shard driven through the C ABI.
+
+A step is: enqueue the unscale/overflow/norm pass on the gradient shard,
+(in a multi-rank job: all-reduce the two scalars), enqueue the fused AdamW
+pass, then read the 4-byte overflow flag back to update the loss scale and the
+step counter on the host.  The flag read is the step's only device-to-host
+transfer; the skip itself is decided on the device from the same flag, so the
+kernels never wait for the host.
+"""
+from typing import Callable, Optional
+
+import torch
+
+from . import (AdamHyper, LossScaler, dtype_code, zero_loss_scaler_update, zero_norm_workspace_bytes,
+               zero_shard_adam_step, zero_shard_unscale_norm_overflow)
+
+
+class ShardAdam:
+    def __init__(self, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, *,
+                 lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=0.0,
+                 scaler: Optional[LossScaler] = None, applied_steps: int = 0):
+        n = master.numel()
+        for t in (master, exp_avg, exp_avg_sq):
+            if t.dtype != torch.float32 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
+                raise ValueError("master / exp_avg / exp_avg_sq must be contiguous fp32 device tensors of equal size")
+        self.master, self.exp_avg, self.exp_avg_sq, self.n = master, exp_avg, exp_avg_sq, n
+        self.hyper = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+                          max_grad_norm=max_grad_norm)
+        self.scaler = scaler if scaler is not None else LossScaler.static(1.0)
+        self.t = applied_steps
+        dev = master.device
+        self.workspace = torch.empty(zero_norm_workspace_bytes(n), dtype=torch.uint8, device=dev)
+        self.sqnorm = torch.empty(1, dtype=torch.float64, device=dev)
+        self.overflow = torch.empty(1, dtype=torch.int32, device=dev)
+        self._flag_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        self._flag_ready = torch.cuda.Event()
+
+    def unscale_norm(self, grad: torch.Tensor) -> None:
+        """Enqueue steps 1-2: self.sqnorm, self.overflow <- this shard's values."""
+        zero_shard_unscale_norm_overflow(grad, 1.0 / self.scaler.scale, self.sqnorm, self.overflow, self.workspace)
+
+    def apply(self, grad: torch.Tensor, param_out: Optional[torch.Tensor], global_sqnorm=None,
+              global_overflow=None) -> None:
+        """Enqueue steps 3-4 for step index t+1 (skipped on device on overflow)."""
+        hp = AdamHyper(step=self.t + 1, inv_loss_scale=1.0 / self.scaler.scale, **self.hyper)
+        zero_shard_adam_step(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out, hp,
+                             self.sqnorm if global_sqnorm is None else global_sqnorm,
+                             self.overflow if global_overflow is None else global_overflow,
+                             grad_dtype=dtype_code(grad))
+
+    def finish(self, global_overflow: Optional[torch.Tensor] = None) -> bool:
+        """Read the overflow flag, update the loss scale and t; returns skip."""
+        flag = self.overflow if global_overflow is None else global_overflow
+        self._flag_host.copy_(flag, non_blocking=True)
+        self._flag_ready.record()
+        self._flag_ready.synchronize()
+        skip = zero_loss_scaler_update(self.scaler, bool(self._flag_host.item()))
+        if not skip:
+            self.t += 1
+        return skip
+
+    def step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor] = None,
+             allreduce: Optional[Callable[[torch.Tensor, torch.Tensor], None]] = None) -> bool:
+        """One full step.  `allreduce(sqnorm, overflow)`, if given, must turn
+        this rank's two scalars into the data-parallel sum / OR in place (on
+        one GPU the shard's own values are the global ones).  Returns True if
+        the step was skipped."""
+        self.unscale_norm(grad)
+        if allreduce is not None:
+            allreduce(self.sqnorm, self.overflow)
+        self.apply(grad, param_out)
+        return self.finish()
