@@ -11,10 +11,10 @@
 // clipping is global max-norm clipping (Pascanu et al. 2013).
 //
 // Both passes are HBM-bandwidth bound elementwise streams (no contraction, so
-// no MFMA): every thread moves whole 16-byte vectors (8 16-bit values, or 4
-// fp32 values), consecutive lanes touch consecutive vectors so each wave64
-// access is a 1 KiB contiguous run, and the streams are read once, so loads
-// and stores are marked non-temporal.
+// no MFMA): threads move whole vectors (16 bytes of fp32, 8 or 16 bytes of
+// 16-bit values), consecutive lanes touch consecutive vectors so every wave64
+// access instruction is one contiguous run, and the streams are read once, so
+// loads and stores are marked non-temporal.
 //
 //  pass 1  sqnorm_partials + sqnorm_finalize: reads the 2-byte gradient once
 //          (2 B/element), ORs an exponent-bits inf/NaN test, sums exact fp64
@@ -22,7 +22,10 @@
 //          xor-shuffles and across the block's four waves through LDS, then a
 //          one-block kernel combines the block partials in a fixed order.
 //  pass 2  adam_update: 28 B/element (2 grad + 4 master + 4 m + 4 v read,
-//          4 + 4 + 4 written back, 2 param written).
+//          4 + 4 + 4 written back, 2 param written).  One wave64 per
+//          workgroup, lane l owning 4 consecutive elements, so each access
+//          instruction is one contiguous, fully used run of cache lines; the
+//          number of resident waves per CU is capped (see kAdamLdsReserve).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -36,13 +39,22 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;              // four wave64s
 constexpr int kWaves = kBlock / 64;
 constexpr int kNormMaxBlocks = 2048;     // 8 blocks per CU on 256 CUs
 constexpr int kNormVecsPerThread = 8;    // grow the grid before this is exceeded
-constexpr int kAdamUnroll = 2;           // 16-byte vectors per thread per tile
-constexpr int64_t kMaxGrid = 1 << 22;    // grid x stays far below 2^32 work-items
+// fused update: one wave64 per workgroup, 4 consecutive elements per lane
+constexpr int kAdamThreads = 64;
+constexpr int kAdamTask = 4 * kAdamThreads;             // elements per workgroup per task
+// Occupancy cap.  With eight streams in flight HBM sustains more bytes per
+// second when fewer waves compete for DRAM rows: 12 KiB of LDS per
+// workgroup leaves room for 13 resident one-wave workgroups per CU (160 KiB
+// of LDS per CU on gfx950).  Chosen by measurement on MI355X over 0-32 KiB
+// (0 KiB: ~75% of HBM peak; 12 KiB: ~82%; 32 KiB: ~55%).
+constexpr size_t kAdamLdsReserve = 12 * 1024;
+constexpr int64_t kAdamMaxGrid = (int64_t(1) << 26) - 1;   // grid * 64 work-items < 2^32
 
 // ---------------------------------------------------------------- 16-bit helpers
 
@@ -204,10 +216,6 @@ struct AdamCoef {
     double inv_scale, max_norm;
 };
 
-struct Elem {
-    float p, m, v;
-};
-
 __device__ __forceinline__ void adam_elem(const AdamCoef& c, float gscale, float graw, float& p, float& m,
                                           float& v) {
     const float g = graw * gscale;
@@ -218,12 +226,15 @@ __device__ __forceinline__ void adam_elem(const AdamCoef& c, float gscale, float
 }
 
 template <int GDT, int PDT, bool WRITE_P>
-__global__ __launch_bounds__(kBlock) void adam_update(float* __restrict__ P, float* __restrict__ M,
-                                                      float* __restrict__ V,
-                                                      const uint16_t* __restrict__ G,
-                                                      uint16_t* __restrict__ Pout, int64_t n, AdamCoef c,
-                                                      const double* __restrict__ d_sq,
-                                                      const int32_t* __restrict__ d_ovf) {
+__global__ __launch_bounds__(kAdamThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
+                                                            float* __restrict__ V,
+                                                            const uint16_t* __restrict__ G,
+                                                            uint16_t* __restrict__ Pout, int64_t n, AdamCoef c,
+                                                            const double* __restrict__ d_sq,
+                                                            const int32_t* __restrict__ d_ovf) {
+    // Dynamic LDS reserved by the launcher only to cap how many of these
+    // workgroups (one wave each) are resident per CU; it is never read.
+    extern __shared__ float occupancy_pad[];
     // skipped step: the whole grid sees the same flag and writes nothing
     if (d_ovf != nullptr && *d_ovf != 0) return;
     float gscale = c.gscale_fixed;
@@ -233,83 +244,54 @@ __global__ __launch_bounds__(kBlock) void adam_update(float* __restrict__ P, flo
         if (!(coef < 1.0)) coef = 1.0;
         gscale = (float)(c.inv_scale * coef);
     }
-    const int64_t nvec = n >> 3;
-    const int tail_n = (int)(n & 7);
-    const int64_t nwork = nvec + (tail_n ? 1 : 0);   // the ragged tail is one extra work item
-    constexpr int64_t kTile = (int64_t)kBlock * kAdamUnroll;
-
-    for (int64_t tile = blockIdx.x; tile * kTile < nwork; tile += gridDim.x) {
-        const int64_t base = tile * kTile + threadIdx.x;
-        u32x4 gq[kAdamUnroll];
-        f32x4 p4[kAdamUnroll][2], m4[kAdamUnroll][2], v4[kAdamUnroll][2];
+    const int lane = threadIdx.x;
+    const int64_t ntasks = (n + kAdamTask - 1) / kAdamTask;
+    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
+        // lane owns elements [e0, e0 + 4): every access instruction of the wave
+        // covers one contiguous run (1 KiB per fp32 stream, 512 B per 16-bit one)
+        const int64_t e0 = t * kAdamTask + 4 * lane;
+        if (e0 + 4 <= n) {
+            const int64_t q = e0 >> 2;
+            f32x4* p4 = reinterpret_cast<f32x4*>(P) + q;
+            f32x4* m4 = reinterpret_cast<f32x4*>(M) + q;
+            f32x4* v4 = reinterpret_cast<f32x4*>(V) + q;
+            f32x4 p = ld_stream(p4), m = ld_stream(m4), v = ld_stream(v4);
+            const u32x2 gq = ld_stream(reinterpret_cast<const u32x2*>(G) + q);
+            float g[4];
+            unpack2<GDT>(gq[0], g[0], g[1]);
+            unpack2<GDT>(gq[1], g[2], g[3]);
 #pragma unroll
-        for (int u = 0; u < kAdamUnroll; ++u) {
-            const int64_t i = base + (int64_t)u * kBlock;
-            if (i < nvec) {
-                gq[u] = ld_stream(reinterpret_cast<const u32x4*>(G) + i);
-                const f32x4* p = reinterpret_cast<const f32x4*>(P) + 2 * i;
-                const f32x4* m = reinterpret_cast<const f32x4*>(M) + 2 * i;
-                const f32x4* v = reinterpret_cast<const f32x4*>(V) + 2 * i;
-                p4[u][0] = ld_stream(p);
-                p4[u][1] = ld_stream(p + 1);
-                m4[u][0] = ld_stream(m);
-                m4[u][1] = ld_stream(m + 1);
-                v4[u][0] = ld_stream(v);
-                v4[u][1] = ld_stream(v + 1);
+            for (int k = 0; k < 4; ++k) {
+                float pk = p[k], mk = m[k], vk = v[k];
+                adam_elem(c, gscale, g[k], pk, mk, vk);
+                p[k] = pk;
+                m[k] = mk;
+                v[k] = vk;
             }
-        }
-#pragma unroll
-        for (int u = 0; u < kAdamUnroll; ++u) {
-            const int64_t i = base + (int64_t)u * kBlock;
-            if (i < nvec) {
-                float g[8];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) unpack2<GDT>(gq[u][k], g[2 * k], g[2 * k + 1]);
-                u32x4 out16;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        float p = p4[u][h][k], m = m4[u][h][k], v = v4[u][h][k];
-                        adam_elem(c, gscale, g[4 * h + k], p, m, v);
-                        p4[u][h][k] = p;
-                        m4[u][h][k] = m;
-                        v4[u][h][k] = v;
-                    }
-                }
-                if constexpr (WRITE_P) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float a = p4[u][k >> 1][(2 * k) & 3], b = p4[u][k >> 1][(2 * k + 1) & 3];
-                        out16[k] = to16<PDT>(a) | (to16<PDT>(b) << 16);
-                    }
-                }
-                f32x4* p = reinterpret_cast<f32x4*>(P) + 2 * i;
-                f32x4* m = reinterpret_cast<f32x4*>(M) + 2 * i;
-                f32x4* v = reinterpret_cast<f32x4*>(V) + 2 * i;
-                st_stream(p4[u][0], p);
-                st_stream(p4[u][1], p + 1);
-                st_stream(m4[u][0], m);
-                st_stream(m4[u][1], m + 1);
-                st_stream(v4[u][0], v);
-                st_stream(v4[u][1], v + 1);
-                if constexpr (WRITE_P) st_stream(out16, reinterpret_cast<u32x4*>(Pout) + i);
-            } else if (i == nvec && tail_n) {
-                // ragged tail: fewer than 8 elements, scalar accesses
-                for (int k = 0; k < tail_n; ++k) {
-                    const int64_t e = nvec * 8 + k;
-                    const uint32_t h = G[e];
-                    const float graw = GDT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
-                    float p = P[e], m = M[e], v = V[e];
-                    adam_elem(c, gscale, graw, p, m, v);
-                    P[e] = p;
-                    M[e] = m;
-                    V[e] = v;
-                    if constexpr (WRITE_P) Pout[e] = (uint16_t)to16<PDT>(p);
-                }
+            st_stream(p, p4);
+            st_stream(m, m4);
+            st_stream(v, v4);
+            if constexpr (WRITE_P) {
+                u32x2 out16;
+                out16[0] = to16<PDT>(p[0]) | (to16<PDT>(p[1]) << 16);
+                out16[1] = to16<PDT>(p[2]) | (to16<PDT>(p[3]) << 16);
+                st_stream(out16, reinterpret_cast<u32x2*>(Pout) + q);
+            }
+        } else if (e0 < n) {
+            // ragged tail: the last 1-3 elements, scalar accesses
+            for (int64_t e = e0; e < n; ++e) {
+                const uint32_t h = G[e];
+                const float graw = GDT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+                float p = P[e], m = M[e], v = V[e];
+                adam_elem(c, gscale, graw, p, m, v);
+                P[e] = p;
+                M[e] = m;
+                V[e] = v;
+                if constexpr (WRITE_P) Pout[e] = (uint16_t)to16<PDT>(p);
             }
         }
     }
+    if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -330,7 +312,7 @@ int launch_status(const char* what) {
 template <int GDT, int PDT, bool WRITE_P>
 void launch_adam(dim3 grid, hipStream_t s, float* P, float* M, float* V, const void* G, void* Pout,
                  int64_t n, const AdamCoef& c, const double* d_sq, const int32_t* d_ovf) {
-    hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kBlock), 0, s, P, M, V,
+    hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kAdamThreads), kAdamLdsReserve, s, P, M, V,
                        static_cast<const uint16_t*>(G), static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
 }
 
@@ -445,12 +427,9 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
     c.inv_scale = h.inv_loss_scale;
     c.max_norm = clip ? h.max_grad_norm : 0.0;
 
-    const int64_t nvec = n >> 3;
-    const int64_t nwork = nvec + ((n & 7) ? 1 : 0);
-    const int64_t tile = (int64_t)kBlock * kAdamUnroll;
-    int64_t ntiles = (nwork + tile - 1) / tile;
-    if (ntiles > kMaxGrid) ntiles = kMaxGrid;   // the kernel strides over the rest
-    const dim3 grid((unsigned)ntiles);
+    int64_t ntasks = (n + kAdamTask - 1) / kAdamTask;
+    if (ntasks > kAdamMaxGrid) ntasks = kAdamMaxGrid;   // the kernel strides over the rest
+    const dim3 grid((unsigned)ntasks);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const bool wp = param_out != nullptr;
     const int pdt = wp ? param_dtype : ZERO_F16;
