@@ -73,33 +73,29 @@ def upload_inputs(w, begin, S, grad_dtype, block_chunks=16):
     return P, M, V, G
 
 
-def cpu_baseline(w, begin, S, target_s=12.0):
-    """The CPU oracle's full step (norm + AdamW) on a bounded contiguous
-    sample of the same shard, single process."""
-    import numpy as np  # noqa: F401
-
+def cpu_baseline(w, begin, S, target_s=10.0, block=1 << 24):
+    """The CPU oracle's full step (exact norm + AdamW) on a bounded sample of
+    the same shard: consecutive blocks of 2^24 parameters from its start,
+    one process, until at least `target_s` seconds of oracle time."""
     import oracle
     import workloads as W
 
-    def run(n):
-        p, m, v, g = W.shard_inputs(w, begin, n)
+    inv = 1.0 / w.loss_scale
+    done, spent = 0, 0.0
+    while spent < target_s and done < S:
+        n = min(block, S - done)
+        p, m, v, g = W.shard_inputs(w, begin + done, n)
         t0 = time.perf_counter()
-        inv = 1.0 / w.loss_scale
         sq, ovf = oracle.shard_sqnorm_overflow(g, w.grad_dtype, inv)
         oracle.shard_step(p, m, v, g, w.grad_dtype, w.param_dtype, global_sq=sq, global_overflow=ovf,
                           inv_loss_scale=inv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
                           beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.step)
-        return time.perf_counter() - t0
-
-    n0 = min(S, 1 << 18)
-    run(n0)                                    # warm the allocator
-    t = run(n0)
-    n = int(min(S, max(n0, n0 * target_s / max(t, 1e-9))))
-    n = min(n, 1 << 26)
-    t = run(n)
-    return {"value": n / t, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} params of the same shard, one step (exact norm + AdamW, float64 NumPy), "
-                      f"single process, {t:.1f} s"}
+        spent += time.perf_counter() - t0
+        done += n
+    return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of the shard's {S} params in blocks of {block}, one step each "
+                      f"(exact norm + AdamW, float64 NumPy, one process); {spent:.1f} s of oracle time, "
+                      f"input generation excluded"}
 
 
 def main():
@@ -177,7 +173,9 @@ def main():
     step_gbps = STEP_BYTES_PER_PARAM * S / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
 
-    # practical ceiling: torch's device copy over the same 14 B/param read + 14 B/param write
+    # context: torch's device-to-device copy (the runtime's blit kernel) over
+    # the same 14 B/param read + 14 B/param write; also the known-size copy
+    # that scales the HBM byte counters
     src = torch.empty(S * 14 // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -216,7 +214,7 @@ def main():
                      "algorithmic_bytes": ADAM_BYTES_PER_PARAM * S, "avg_ms": adam_avg,
                      "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9)},
         "norm_pass": {"avg_ms": mean(norm_ms), "gbps": NORM_BYTES_PER_PARAM * S / (mean(norm_ms) * 1e-3) / 1e9},
-        "copy_ceiling_gbps": copy_gbps,
+        "torch_copy_gbps": copy_gbps,
         "skipped_steps": skipped,
         "cpu_baseline": cpu,
     }

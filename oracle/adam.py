@@ -31,35 +31,40 @@ import numpy as np
 
 from .formats import FORMATS, decode16, encode16_rne, is_nonfinite16
 
-_EXACT_CHUNK = 1 << 24
+def _magnitude_counts(bits: np.ndarray, fmt: str) -> np.ndarray:
+    """How many elements carry each 16-bit magnitude pattern (sign dropped):
+    counts[p] for p in [0, 0x8000)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return np.bincount(b & np.uint16(0x7FFF), minlength=0x8000).astype(np.int64)
 
 
-def _sum_squares_exact(bits: np.ndarray, fmt: str) -> Fraction:
-    """Exact sum of squares of the finite 16-bit values, as a rational.
+def _sum_squares_from_counts(counts: np.ndarray, fmt: str) -> Fraction:
+    """Exact sum of squares of the finite values given by a magnitude
+    histogram: sum over patterns p of counts[p] * value(p)^2.
 
-    Each finite value is +-M * 2^E with integer significand M.  Its square is
-    M^2 * 2^(2E); summing the integers M^2 per exponent E is exact (every
-    partial sum is an integer below 2^53 for chunks of 2^24 elements), and the
-    per-exponent sums are combined in exact rational arithmetic.
+    A finite pattern with exponent field e and fraction f has value
+    M * 2^E with integer M (f for e = 0, 2^mbits + f otherwise) and
+    E = max(e, 1) - bias - mbits; its square M^2 * 2^(2E) is summed as an
+    integer multiple of 2^(2 Emin), Emin = 1 - bias - mbits.
     """
     ebits, mbits, bias = FORMATS[fmt]
     emax_field = (1 << ebits) - 1
-    emin = 1 - bias
-    total = Fraction(0)
-    b_all = np.asarray(bits)
-    for s in range(0, b_all.size, _EXACT_CHUNK):
-        b = b_all[s:s + _EXACT_CHUNK].astype(np.int64) & 0xFFFF
-        e = (b >> mbits) & emax_field
-        f = b & ((1 << mbits) - 1)
-        finite = e != emax_field
-        e, f = e[finite], f[finite]
-        M = np.where(e == 0, f, f + (1 << mbits))
-        E = np.where(e == 0, emin - mbits, e - bias - mbits)   # value = M * 2^E
-        idx = E - (emin - mbits)                                # >= 0
-        per_exp = np.bincount(idx, weights=(M * M).astype(np.float64))
-        for i in np.nonzero(per_exp)[0]:
-            total += Fraction(int(per_exp[i])) * Fraction(2) ** (2 * (int(i) + emin - mbits))
-    return total
+    e_min = 1 - bias - mbits
+    total = 0
+    for p in np.nonzero(counts)[0]:
+        p = int(p)
+        e, f = p >> mbits, p & ((1 << mbits) - 1)
+        if e == emax_field:
+            continue                     # inf / NaN: handled by the caller
+        M = f if e == 0 else f + (1 << mbits)
+        E = max(e, 1) - bias - mbits
+        total += int(counts[p]) * M * M << (2 * (E - e_min))
+    return Fraction(total) * Fraction(2) ** (2 * e_min)
+
+
+def _sum_squares_exact(bits: np.ndarray, fmt: str) -> Fraction:
+    """Exact sum of squares of the finite 16-bit values, as a rational."""
+    return _sum_squares_from_counts(_magnitude_counts(bits, fmt), fmt)
 
 
 def shard_sqnorm_overflow(grad_bits: np.ndarray, fmt: str, inv_loss_scale: float) -> Tuple[float, bool]:
@@ -85,7 +90,7 @@ def global_sqnorm_overflow(shards: Iterable[np.ndarray], fmt: str,
                            inv_loss_scale: float) -> Tuple[float, bool]:
     """The data-parallel reduction of the per-rank results: the global sum of
     squares over all shards (exact, one rounding) and the OR of the flags."""
-    total, overflow, has_nan = Fraction(0), False, False
+    counts, overflow, has_nan = np.zeros(0x8000, np.int64), False, False
     for bits in shards:
         bits = np.asarray(bits)
         bad = is_nonfinite16(bits, fmt)
@@ -93,10 +98,10 @@ def global_sqnorm_overflow(shards: Iterable[np.ndarray], fmt: str,
             overflow = True
             has_nan |= bool(np.isnan(decode16(bits[bad], fmt)).any())
         else:
-            total += _sum_squares_exact(bits, fmt)
+            counts += _magnitude_counts(bits, fmt)
     if overflow:
         return (math.nan if has_nan else math.inf), True
-    return float(total * Fraction(inv_loss_scale) ** 2), False
+    return float(_sum_squares_from_counts(counts, fmt) * Fraction(inv_loss_scale) ** 2), False
 
 
 def clip_coefficient(sq: float, max_grad_norm: float) -> float:

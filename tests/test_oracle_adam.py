@@ -52,6 +52,24 @@ def test_sqnorm_closed_form():
             assert not ovf and sq == n * 2.0**(-2 * k) * 0.25
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_sqnorm_every_pattern_exhaustive(fmt):
+    """Every finite 16-bit pattern (both signs), and the subnormals alone:
+    the oracle's sum of squares equals math.fsum of the library-decoded
+    squares (both are the correctly rounded exact sum)."""
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = _lib_vals(allp, fmt)
+    finite = np.isfinite(v)
+    sq, ovf = shard_sqnorm_overflow(allp[finite], fmt, 1.0)
+    assert not ovf and sq == math.fsum((v[finite] ** 2).tolist())
+    sub = allp[(allp & 0x7FFF) < (0x400 if fmt == "f16" else 0x80)]
+    vs = _lib_vals(sub, fmt)
+    for inv in (1.0, 2.0**-16, 3.0):
+        sq, _ = shard_sqnorm_overflow(sub, fmt, inv)
+        assert sq == math.fsum(((vs * inv) ** 2).tolist()) or \
+            abs(sq - math.fsum(((vs * inv) ** 2).tolist())) <= 1e-15 * sq
+
+
 def test_sqnorm_empty_and_zero():
     assert shard_sqnorm_overflow(np.zeros(0, np.uint16), "f16", 1.0) == (0.0, False)
     assert shard_sqnorm_overflow(np.zeros(100, np.uint16), "bf16", 1.0) == (0.0, False)

@@ -21,6 +21,7 @@
 //          squares per thread in a fixed order, reduces within a wave by
 //          xor-shuffles and across the block's four waves through LDS, then a
 //          one-block kernel combines the block partials in a fixed order.
+//          Only the first block touches the ragged remainder.
 //  pass 2  adam_update: 28 B/element (2 grad + 4 master + 4 m + 4 v read,
 //          4 + 4 + 4 written back, 2 param written).  One wave64 per
 //          workgroup, lane l owning 4 consecutive elements, so each access
@@ -43,8 +44,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;              // four wave64s
 constexpr int kWaves = kBlock / 64;
-constexpr int kNormMaxBlocks = 2048;     // 8 blocks per CU on 256 CUs
-constexpr int kNormVecsPerThread = 8;    // grow the grid before this is exceeded
+// norm pass: 512 blocks of 256 threads (2 per CU), each step of the
+// grid-stride loop reads a 16 KiB chunk per block; chosen by measurement on
+// MI355X (~7.1 TB/s on a 2 GB gradient shard)
+constexpr int kNormMaxBlocks = 512;
+constexpr int kNormUnroll = 4;                          // 16-byte loads in flight per thread
+constexpr int64_t kNormChunk = (int64_t)kBlock * kNormUnroll;   // vectors per block per step
 // fused update: one wave64 per workgroup, 4 consecutive elements per lane
 constexpr int kAdamThreads = 64;
 constexpr int kAdamTask = 4 * kAdamThreads;             // elements per workgroup per task
@@ -73,13 +78,6 @@ __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
         lo = __uint_as_float(w << 16);
         hi = __uint_as_float(w & 0xFFFF0000u);
     }
-}
-
-// 1 if either half of w is inf/NaN (exponent field all ones)
-template <int DT>
-__device__ __forceinline__ uint32_t nonfinite2(uint32_t w) {
-    constexpr uint32_t m = DT == ZERO_F16 ? 0x7C00u : 0x7F80u;
-    return (uint32_t)((w & m) == m) | (uint32_t)(((w >> 16) & m) == m);
 }
 
 // round-to-nearest-even float -> 16-bit bits (hardware conversion under the
@@ -125,19 +123,34 @@ __device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad, double*
 
 // ---------------------------------------------------------------- pass 1
 
+// Per 32-bit word of two 16-bit values: (w & E) + C sets bit 15 (bit 31) iff
+// the low (high) half has an all-ones exponent field, i.e. is inf or NaN;
+// no carry crosses from the low half into the high half.  OR-accumulating
+// these words and testing kNonfiniteBits at the end is an exact inf/NaN test.
+template <int DT>
+struct Exp16 {
+    static constexpr uint32_t mask2 = DT == ZERO_F16 ? 0x7C007C00u : 0x7F807F80u;
+    static constexpr uint32_t carry2 = DT == ZERO_F16 ? 0x04000400u : 0x00800080u;
+};
+constexpr uint32_t kNonfiniteBits = 0x80008000u;
+
 template <int DT>
 __device__ __forceinline__ void accumulate_vec(u32x4 q, double& acc, uint32_t& bad) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         float lo, hi;
         unpack2<DT>(q[k], lo, hi);
-        bad |= nonfinite2<DT>(q[k]);
+        bad |= (q[k] & Exp16<DT>::mask2) + Exp16<DT>::carry2;
         const double a = (double)lo, b = (double)hi;   // exact; squares exact in fp64
         acc = fma(a, a, acc);
         acc = fma(b, b, acc);
     }
 }
 
+// Grid-stride over chunks of kNormChunk consecutive 16-byte vectors: at every
+// step the grid reads one contiguous window, and each wave's four loads are
+// consecutive 1 KiB runs.  The grid size depends only on n, so the summation
+// order (and the result) is the same on every run.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restrict__ g, int64_t nvec,
                                                           const uint16_t* __restrict__ tail, int tail_n,
@@ -147,27 +160,30 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restric
     __shared__ uint32_t s_bad[kWaves];
     double acc = 0.0;
     uint32_t bad = 0;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    // four independent 16-byte loads in flight per thread
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        const u32x4 a = ld_stream(g + i), b = ld_stream(g + i + stride);
-        const u32x4 c = ld_stream(g + i + 2 * stride), d = ld_stream(g + i + 3 * stride);
-        accumulate_vec<DT>(a, acc, bad);
-        accumulate_vec<DT>(b, acc, bad);
-        accumulate_vec<DT>(c, acc, bad);
-        accumulate_vec<DT>(d, acc, bad);
+    const int64_t nchunks = nvec / kNormChunk;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const u32x4* base = g + c * kNormChunk + threadIdx.x;
+        u32x4 q[kNormUnroll];
+#pragma unroll
+        for (int u = 0; u < kNormUnroll; ++u) q[u] = ld_stream(base + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kNormUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
     }
-    for (; i < nvec; i += stride) accumulate_vec<DT>(ld_stream(g + i), acc, bad);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        for (int k = 0; k < tail_n; ++k) {
-            const uint32_t h = tail[k];
-            const float x = DT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
-            bad |= nonfinite2<DT>(h);
-            const double a = (double)x;
-            acc = fma(a, a, acc);
+    if (blockIdx.x == 0) {
+        // fewer than kNormChunk vectors left over, then fewer than 8 elements
+        for (int64_t i = nchunks * kNormChunk + threadIdx.x; i < nvec; i += kBlock)
+            accumulate_vec<DT>(ld_stream(g + i), acc, bad);
+        if (threadIdx.x == 0) {
+            for (int k = 0; k < tail_n; ++k) {
+                const uint32_t h = tail[k];
+                const float x = DT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+                bad |= (h & Exp16<DT>::mask2) + Exp16<DT>::carry2;
+                const double a = (double)x;
+                acc = fma(a, a, acc);
+            }
         }
     }
+    bad = (bad & kNonfiniteBits) != 0;
     block_reduce(acc, bad, s_sq, s_bad);
     if (threadIdx.x == 0) {
         part_sq[blockIdx.x] = acc;
@@ -196,8 +212,7 @@ __global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restri
 }
 
 int norm_blocks(int64_t n) {
-    const int64_t nvec = n / 8;
-    int64_t b = (nvec + (int64_t)kBlock * kNormVecsPerThread - 1) / ((int64_t)kBlock * kNormVecsPerThread);
+    int64_t b = (n / 8) / kNormChunk;      // one block per full chunk, at most kNormMaxBlocks
     if (b < 1) b = 1;
     if (b > kNormMaxBlocks) b = kNormMaxBlocks;
     return (int)b;
