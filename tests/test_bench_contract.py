@@ -1,0 +1,27 @@
+"""bench.py contract checks that need no GPU."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "ONE GPU" in r.stderr and r.stdout == ""
+
+
+def test_counter_summary_is_tied_to_kernel_source():
+    sys.path.insert(0, ROOT)
+    import bench
+    data = json.load(open(os.path.join(ROOT, "profiles", "hbm_counters.json")))
+    rec = data["adam_update"]["gpt_1t_nd1024_last_rank"]
+    # the algorithmic bytes recorded with the counters are 28 B/param of the shard
+    assert rec["algorithmic_bytes"] == 28 * 976077312
+    if rec["kernel_sha256_16"] == bench.kernel_source_hash():
+        assert bench.measured_traffic("gpt_1t_nd1024_last_rank") == rec["bytes_per_launch"]
+    else:
+        assert bench.measured_traffic("gpt_1t_nd1024_last_rank") is None
