@@ -16,6 +16,8 @@ shard.  The pages give no update formula.  The steps are read as:
      root) and decoupled weight decay scaled by the learning rate
      (Loshchilov & Hutter 2019 with the schedule multiplier equal to lr);
   4. round the updated fp32 master weight to the 16-bit parameter copy.
+With gradient accumulation the step consumes the fp32 gradient copy instead
+of the 16-bit gradient (format 'f32', already unscaled).
 A step whose gradient holds any inf/NaN is skipped: no state changes, the step
 counter does not advance and the loss scale is reduced.
 
@@ -67,6 +69,31 @@ def _sum_squares_exact(bits: np.ndarray, fmt: str) -> Fraction:
     return _sum_squares_from_counts(_magnitude_counts(bits, fmt), fmt)
 
 
+def _grad_f64(grad, fmt: str) -> np.ndarray:
+    """Gradient values as float64: decoded 16-bit patterns, or an fp32
+    gradient (fmt 'f32', e.g. an fp32 accumulation buffer) widened exactly."""
+    if fmt == "f32":
+        return np.asarray(grad, dtype=np.float32).astype(np.float64)
+    return decode16(grad, fmt)
+
+
+def _sqnorm_overflow_f32(g32: np.ndarray, inv_loss_scale: float, chunk: int = 1 << 24) -> Tuple[float, bool]:
+    """fp32 gradient: overflow = any non-finite element; sq = sum of
+    (g * inv_loss_scale)^2.  Each square of an fp32 value times a power of two
+    is exact in float64; each 2^24-element chunk is summed pairwise in float64
+    and the chunk sums are combined with math.fsum, so the relative error is
+    below 1e-14."""
+    x = np.asarray(g32, dtype=np.float32)
+    finite = np.isfinite(x)
+    if not finite.all():
+        return (math.nan if np.isnan(x).any() else math.inf), True
+    parts = []
+    for s in range(0, x.size, chunk):
+        y = x[s:s + chunk].astype(np.float64) * inv_loss_scale
+        parts.append(float(np.sum(y * y)))
+    return math.fsum(parts), False
+
+
 def shard_sqnorm_overflow(grad_bits: np.ndarray, fmt: str, inv_loss_scale: float) -> Tuple[float, bool]:
     """(sq, overflow) for one gradient shard.
 
@@ -76,6 +103,8 @@ def shard_sqnorm_overflow(grad_bits: np.ndarray, fmt: str, inv_loss_scale: float
     to float64; +inf if the shard holds an inf and no NaN, NaN if it holds a
     NaN.
     """
+    if fmt == "f32":
+        return _sqnorm_overflow_f32(grad_bits, inv_loss_scale)
     bits = np.asarray(grad_bits)
     bad = is_nonfinite16(bits, fmt)
     overflow = bool(bad.any())
@@ -90,6 +119,11 @@ def global_sqnorm_overflow(shards: Iterable[np.ndarray], fmt: str,
                            inv_loss_scale: float) -> Tuple[float, bool]:
     """The data-parallel reduction of the per-rank results: the global sum of
     squares over all shards (exact, one rounding) and the OR of the flags."""
+    if fmt == "f32":
+        parts = [_sqnorm_overflow_f32(g, inv_loss_scale) for g in shards]
+        if any(o for _, o in parts):
+            return (math.nan if any(math.isnan(q) for q, _ in parts) else math.inf), True
+        return math.fsum(q for q, _ in parts), False
     counts, overflow, has_nan = np.zeros(0x8000, np.int64), False, False
     for bits in shards:
         bits = np.asarray(bits)
@@ -133,7 +167,7 @@ def adam_update(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
     p = np.asarray(master, dtype=np.float64)
     m = np.asarray(exp_avg, dtype=np.float64)
     v = np.asarray(exp_avg_sq, dtype=np.float64)
-    g = decode16(grad_bits, grad_fmt) * gscale
+    g = _grad_f64(grad_bits, grad_fmt) * gscale
     m_new = beta1 * m + (1.0 - beta1) * g
     v_new = beta2 * v + (1.0 - beta2) * g * g
     m_hat = m_new / (1.0 - beta1 ** step)
@@ -142,6 +176,24 @@ def adam_update(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
     master32 = p_new.astype(np.float32)
     param = encode16_rne(master32, param_fmt) if param_fmt is not None else None
     return master32, m_new.astype(np.float32), v_new.astype(np.float32), param
+
+
+def grad_accumulate(acc32: Optional[np.ndarray], grad_bits: np.ndarray, fmt: str,
+                    inv_loss_scale: float) -> Tuple[np.ndarray, bool]:
+    """One micro-batch into the fp32 gradient copy.
+
+    [Explainer, Ch.02 "The Three Stages", memory-per-parameter list: an fp16
+    gradient plus its fp32 copy]: the copy accumulates the unscaled 16-bit
+    micro-batch gradients,
+        acc <- float32(acc + g * inv_loss_scale)      (acc None: start at 0)
+    with the sum formed in float64 (exact whenever the two exponents are
+    within 29 binades, true for gradients of one model) and rounded once to
+    float32.  Returns (new acc, overflow) where overflow flags an inf/NaN in
+    this micro-batch's 16-bit input.
+    """
+    t = decode16(grad_bits, fmt) * inv_loss_scale
+    base = 0.0 if acc32 is None else np.asarray(acc32, dtype=np.float32).astype(np.float64)
+    return (base + t).astype(np.float32), bool(is_nonfinite16(grad_bits, fmt).any())
 
 
 @dataclass(frozen=True)
