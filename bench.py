@@ -26,6 +26,11 @@ PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E, published
 ADAM_BYTES_PER_PARAM = 28           # 2 grad + 3x4 read + 3x4 write + 2 param
 NORM_BYTES_PER_PARAM = 2            # gradient read once
 STEP_BYTES_PER_PARAM = ADAM_BYTES_PER_PARAM + NORM_BYTES_PER_PARAM
+# fp32 gradient-accumulation path: the step reads the 4-byte fp32 copy
+ADAM_F32_BYTES_PER_PARAM = 30
+NORM_F32_BYTES_PER_PARAM = 4
+ACC_FIRST_BYTES_PER_PARAM = 6       # 2 read + 4 written
+ACC_BYTES_PER_PARAM = 10            # 2 + 4 read, 4 written
 METRIC = "shard optimizer-step params/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_partition_amd", "csrc", "shard_step.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
@@ -36,15 +41,16 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter summary, or None if absent or taken on a different kernel source."""
+def measured_traffic(key: str, kernel: str = "adam_update"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary for run `key`, or None if absent or taken on a different kernel
+    source."""
     try:
         with open(COUNTERS) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = data.get("adam_update", {}).get(workload)
+    rec = data.get(kernel, {}).get(key)
     if not rec or rec.get("kernel_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
@@ -73,10 +79,11 @@ def upload_inputs(w, begin, S, grad_dtype, block_chunks=16):
     return P, M, V, G
 
 
-def cpu_baseline(w, begin, S, target_s=10.0, block=1 << 24):
-    """The CPU oracle's full step (exact norm + AdamW) on a bounded sample of
-    the same shard: consecutive blocks of 2^24 parameters from its start,
-    one process, until at least `target_s` seconds of oracle time."""
+def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24):
+    """The CPU oracle's full step (exact norm + AdamW; with `accum` > 0, that
+    many micro-batch accumulations into the fp32 copy first) on a bounded
+    sample of the same shard: consecutive blocks of 2^24 parameters from its
+    start, one process, until at least `target_s` seconds of oracle time."""
     import oracle
     import workloads as W
 
@@ -86,15 +93,22 @@ def cpu_baseline(w, begin, S, target_s=10.0, block=1 << 24):
         n = min(block, S - done)
         p, m, v, g = W.shard_inputs(w, begin + done, n)
         t0 = time.perf_counter()
-        sq, ovf = oracle.shard_sqnorm_overflow(g, w.grad_dtype, inv)
-        oracle.shard_step(p, m, v, g, w.grad_dtype, w.param_dtype, global_sq=sq, global_overflow=ovf,
-                          inv_loss_scale=inv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
+        gfmt, ginv = w.grad_dtype, inv
+        if accum:
+            acc = None
+            for _ in range(accum):
+                acc, _ovf = oracle.grad_accumulate(acc, g, w.grad_dtype, inv)
+            g, gfmt, ginv = acc, "f32", 1.0
+        sq, ovf = oracle.shard_sqnorm_overflow(g, gfmt, ginv)
+        oracle.shard_step(p, m, v, g, gfmt, w.param_dtype, global_sq=sq, global_overflow=ovf,
+                          inv_loss_scale=ginv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
                           beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.step)
         spent += time.perf_counter() - t0
         done += n
+    what = f"{accum} accumulations + " if accum else ""
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of the shard's {S} params in blocks of {block}, one step each "
-                      f"(exact norm + AdamW, float64 NumPy, one process); {spent:.1f} s of oracle time, "
+                      f"({what}exact norm + AdamW, float64 NumPy, one process); {spent:.1f} s of oracle time, "
                       f"input generation excluded"}
 
 
@@ -105,6 +119,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt1t",
                     help="tiny | gpt2 | llama7b | gpt100b | gpt1t (default: one rank's shard of a 1T model)")
+    ap.add_argument("--accum", type=int, default=0,
+                    help="micro-batches accumulated into an fp32 gradient copy per step (0: step the 16-bit "
+                         "gradient directly)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -120,7 +137,7 @@ def main():
         # before the GPU is touched (the oracle is host-only)
         import zero_sharded_mixed_partition_amd as Z
         _, S0, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
-        cpu = cpu_baseline(w, w.rank * S0, S0)
+        cpu = cpu_baseline(w, w.rank * S0, S0, accum=args.accum)
         print(f"# cpu baseline {cpu['value']:.4g} params/s", file=sys.stderr, flush=True)
 
     import torch
@@ -137,15 +154,25 @@ def main():
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
                       applied_steps=w.step - 1)
+    K = args.accum
+    A = torch.empty(S, dtype=torch.float32, device="cuda") if K else None
     torch.cuda.synchronize()
 
     def step(ev=None):
+        if K:
+            for k in range(K):
+                if ev is not None and k == K - 1:
+                    ev[3].record()
+                opt.accumulate(A, G, first=(k == 0))
+            if ev is not None:
+                ev[4].record()
+        grad = A if K else G
         if ev is not None:
             ev[0].record()
-        opt.unscale_norm(G)
+        opt.unscale_norm(grad)
         if ev is not None:
             ev[1].record()
-        opt.apply(G, par)
+        opt.apply(grad, par)
         if ev is not None:
             ev[2].record()
         return opt.finish()
@@ -153,7 +180,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     skipped = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -164,14 +191,26 @@ def main():
     print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    norm_ms = sorted(a.elapsed_time(b) for a, b, _ in evs)
-    adam_ms = sorted(b.elapsed_time(c) for _, b, c in evs)
+    norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    adam_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
+    adam_bpp = ADAM_F32_BYTES_PER_PARAM if K else ADAM_BYTES_PER_PARAM
+    norm_bpp = NORM_F32_BYTES_PER_PARAM if K else NORM_BYTES_PER_PARAM
+    acc_bpp = (ACC_FIRST_BYTES_PER_PARAM + ACC_BYTES_PER_PARAM * (K - 1)) if K else 0
+    step_bpp = adam_bpp + norm_bpp + acc_bpp
     adam_avg = mean(adam_ms)
-    adam_gbps = ADAM_BYTES_PER_PARAM * S / (adam_avg * 1e-3) / 1e9
-    step_gbps = STEP_BYTES_PER_PARAM * S / (ms_step * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    adam_gbps = adam_bpp * S / (adam_avg * 1e-3) / 1e9
+    step_gbps = step_bpp * S / (ms_step * 1e-3) / 1e9
+    run_key = w.name + (f"+accum{K}" if K else "")
+    traffic = measured_traffic(run_key)
+    accum_stats = None
+    if K:
+        acc_ms = mean([e[3].elapsed_time(e[4]) for e in evs])     # the last (non-first) accumulation
+        accum_stats = {"micro_batches": K, "kernel": "grad_accumulate", "avg_ms": acc_ms,
+                       "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
+                       "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
+                       "traffic": measured_traffic(run_key, "grad_accumulate")}
 
     # context: torch's device-to-device copy (the runtime's blit kernel) over
     # the same 14 B/param read + 14 B/param write; also the known-size copy
@@ -206,14 +245,16 @@ def main():
                    "flat_offset": begin, "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
                    "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
                    "weight_decay": w.weight_decay, "param_layout": w.param_layout,
-                   "algorithmic_bytes_per_param": STEP_BYTES_PER_PARAM},
+                   "path": f"fp32 gradient accumulation, {K} micro-batches" if K else "16-bit gradient",
+                   "algorithmic_bytes_per_param": step_bpp},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "kernel": "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": ADAM_BYTES_PER_PARAM * S, "avg_ms": adam_avg,
+                     "algorithmic_bytes": adam_bpp * S, "avg_ms": adam_avg,
                      "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9)},
-        "norm_pass": {"avg_ms": mean(norm_ms), "gbps": NORM_BYTES_PER_PARAM * S / (mean(norm_ms) * 1e-3) / 1e9},
+        "norm_pass": {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9},
+        "accumulate": accum_stats,
         "torch_copy_gbps": copy_gbps,
         "skipped_steps": skipped,
         "cpu_baseline": cpu,

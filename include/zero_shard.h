@@ -55,8 +55,11 @@ typedef enum {
     ZERO_EHIP = -5      /* HIP runtime reported an error at launch */
 } zero_status;
 
-/* 16-bit floating-point formats of the gradient and of the parameter copy. */
-enum { ZERO_F16 = 1, ZERO_BF16 = 2 };
+/* Floating-point formats.  ZERO_F16 / ZERO_BF16: 16-bit gradient or
+ * parameter copy.  ZERO_F32: an fp32 gradient (the accumulation buffer of
+ * zero_shard_grad_accumulate), accepted as grad_dtype by
+ * zero_shard_unscale_norm_overflow and zero_shard_adam_step. */
+enum { ZERO_F16 = 1, ZERO_BF16 = 2, ZERO_F32 = 3 };
 
 /* Returns ZERO_SHARD_ABI_VERSION of the built library. */
 int zero_abi_version(void);
@@ -109,7 +112,8 @@ int zero_rank_fragments(const int64_t* dims, const int32_t* ndims, int32_t n_ten
 /* ---------------------------------------------------------------------------
  * Step 1+2: unscale, inf/NaN detection, squared L2 norm of one gradient shard.
  *
- *  grad        device, [n] 16-bit values of format grad_dtype (raw bits)
+ *  grad        device, [n] values of format grad_dtype: 16-bit raw bits
+ *              (ZERO_F16, ZERO_BF16) or fp32 (ZERO_F32)
  *  inv_loss_scale  1 / loss scale (> 0, finite)
  *  d_sqnorm    device, out: one double = sum_i (grad_i * inv_loss_scale)^2
  *              (+inf if the shard holds an inf and no NaN, NaN if it holds
@@ -149,7 +153,9 @@ typedef struct {
 } zero_adam_params;
 
 /*  master, exp_avg, exp_avg_sq  device, [n] float32, updated in place
- *  grad        device, [n] 16-bit gradient (grad_dtype), read only
+ *  grad        device, [n] gradient of format grad_dtype (16-bit, or fp32
+ *              for an accumulated gradient, which is passed already unscaled
+ *              with inv_loss_scale = 1), read only
  *  param_out   device, [n] 16-bit parameter copy (param_dtype) written as
  *              round-to-nearest-even of the new float32 master; NULL skips
  *              the writeback.  For the ZeRO-2 layout pass the rank's slice
@@ -165,7 +171,8 @@ typedef struct {
  * Per element (float32): g = grad * gscale with gscale = float(inv_scale *
  * coef); m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g^2;
  * p = p*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps).
- * Streams 28 bytes per element (2 grad + 3x4 read, 3x4 write + 2 param).
+ * Streams 28 bytes per element (2 grad + 3x4 read, 3x4 write + 2 param;
+ * 30 with an fp32 gradient).
  * grad must not alias master, exp_avg, exp_avg_sq or param_out.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
  * ------------------------------------------------------------------------- */
@@ -173,6 +180,28 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
                          int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
                          const zero_adam_params* hp, const double* d_global_sqnorm,
                          const int32_t* d_global_overflow, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Gradient accumulation into an fp32 copy (explainer, Ch.02 "The Three
+ * Stages", memory per parameter: an fp16 gradient plus its fp32 copy).
+ * For each micro-batch:  acc = (first ? 0 : acc) + grad * inv_loss_scale,
+ * in fp32 with one rounding per element (fused multiply-add).
+ *
+ *  acc         device, [n] float32, updated in place (not read when first)
+ *  grad        device, [n] 16-bit micro-batch gradient (ZERO_F16/ZERO_BF16)
+ *  inv_loss_scale  1 / loss scale of this micro-batch (> 0, finite)
+ *  first       nonzero for the first micro-batch of a step
+ *  d_overflow  device int32 or NULL: set to 1 if this micro-batch holds an
+ *              inf/NaN; never cleared by the library (the caller zeroes it
+ *              when it wants a per-step flag).  Not needed for skipping: an
+ *              inf/NaN propagates into acc, and the norm pass over acc
+ *              (grad_dtype ZERO_F32) reports it.
+ * Streams 10 bytes per element (6 for the first micro-batch).
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+                               double inv_loss_scale, int32_t first, int32_t* d_overflow,
+                               void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Step 2 (scalar, host): dynamic loss scale update after a step.

@@ -129,7 +129,9 @@ def test_device_entry_points_reject_bad_arguments_on_host():
     buf = ctypes.create_string_buffer(64)
     aligned = (ctypes.addressof(buf) + 15) & ~15
     # bad dtype / negative n / null pointers / bad hyperparameters / misalignment
-    assert lib.zero_shard_unscale_norm_overflow(aligned, 3, 8, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
+    # every call below must be rejected by host validation (never a launch on
+    # these host pointers): 7 is not a format code
+    assert lib.zero_shard_unscale_norm_overflow(aligned, 7, 8, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
     assert lib.zero_shard_unscale_norm_overflow(aligned, 1, -1, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
     assert lib.zero_shard_unscale_norm_overflow(aligned, 1, 8, 0.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EINVAL
     assert lib.zero_shard_unscale_norm_overflow(aligned + 2, 1, 8, 1.0, aligned, aligned, aligned, 1 << 20, None) == L.ZERO_EALIGN
@@ -152,6 +154,16 @@ def test_device_entry_points_reject_bad_arguments_on_host():
                                     None, None, None) == L.ZERO_EINVAL
     # n == 0 is a no-op that needs no pointers
     assert lib.zero_shard_adam_step(None, None, None, None, 1, None, 0, 0, A, None, None, None) == L.ZERO_OK
+    # gradient accumulation: fp32 input, bad sizes/scales, misalignment, aliasing
+    acc = lib.zero_shard_grad_accumulate
+    assert acc(aligned, aligned + 16, L.ZERO_F32, 4, 1.0, 1, None, None) == L.ZERO_EINVAL
+    assert acc(aligned, aligned + 16, 7, 4, 1.0, 1, None, None) == L.ZERO_EINVAL
+    assert acc(aligned, aligned + 16, L.ZERO_F16, -1, 1.0, 1, None, None) == L.ZERO_EINVAL
+    assert acc(aligned, aligned + 16, L.ZERO_F16, 4, float("inf"), 1, None, None) == L.ZERO_EINVAL
+    assert acc(aligned + 4, aligned + 16, L.ZERO_F16, 4, 1.0, 1, None, None) == L.ZERO_EALIGN
+    assert acc(aligned, aligned + 16, L.ZERO_F16, 4, 1.0, 1, aligned + 2, None) == L.ZERO_EALIGN
+    assert acc(aligned, aligned + 8 - 8, L.ZERO_BF16, 4, 1.0, 0, None, None) == L.ZERO_EINVAL   # alias
+    assert acc(None, None, L.ZERO_F16, 0, 1.0, 1, None, None) == L.ZERO_OK                       # n == 0
     assert L.lib().zero_last_error() == b""
 
 

@@ -160,3 +160,65 @@ def test_trajectory_with_overflow_full_shard(Z):
     compare_step(got, last, what="after 20 iterations ")
     del P, M, V, G, par
     torch.cuda.empty_cache()
+
+
+def test_fp32_accumulation_full_shard(Z):
+    """The 1T model's last-rank shard (976M params) with 4 micro-batches
+    accumulated into the fp32 gradient copy, then the step on that copy: the
+    oracle accumulates the same micro-batches, takes the norm over the whole
+    fp32 copy and checks the update at sampled elements."""
+    w = W.GPT_1T_LAST_RANK
+    K = 4
+    _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+    begin = w.rank * S
+    real = min(S, max(0, W.real_total(w) - begin))
+    idx = _samples(S, real, k=50_000)
+    P = torch.empty(S, dtype=torch.float32, device="cuda")
+    M = torch.empty_like(P)
+    V = torch.empty_like(P)
+    Gs = [torch.empty(S, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    host = {k: [] for k in ("p", "m", "v", "acc")}
+    inv = 1.0 / w.loss_scale
+
+    def acc_blocks():
+        for lo in range(0, S, BLOCK):
+            n = min(BLOCK, S - lo)
+            p, m, v, _ = W.shard_inputs(w, begin + lo, n)
+            for dst, src in ((P, p), (M, m), (V, v)):
+                dst[lo:lo + n].copy_(torch.from_numpy(src))
+            acc = None
+            for k in range(K):
+                g = W.fill(w, "grad", begin + lo, n, step=500 + k)
+                Gs[k][lo:lo + n].copy_(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16))
+                acc, _ = oracle.grad_accumulate(acc, g, "bf16", inv)
+            sel = idx[(idx >= lo) & (idx < lo + n)] - lo
+            for key, a in (("p", p), ("m", m), ("v", v), ("acc", acc)):
+                host[key].append(a[sel])
+            yield acc
+
+    ref_sq, ref_ovf = oracle.global_sqnorm_overflow(acc_blocks(), "f32", 1.0)
+    h = {k: np.concatenate(a) for k, a in host.items()}
+    A = torch.empty(S, dtype=torch.float32, device="cuda")
+    for k in range(K):
+        Z.zero_shard_grad_accumulate(A, Gs[k], inv, first=(k == 0))
+    del Gs
+    sq, ovf = _norm(Z, A, 1.0)
+    par = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              max_grad_norm=w.max_grad_norm, step=w.step, inv_loss_scale=1.0)
+    Z.zero_shard_adam_step(P, M, V, A, par, Z.AdamHyper(**hp), sq, ovf)
+    torch.cuda.synchronize()
+    assert int(ovf.item()) == int(ref_ovf) == 0
+    check_norm(sq.item(), ref_sq)
+    idx_t = torch.from_numpy(idx).cuda()
+    acc_got = _gather(A, idx_t).cpu().numpy()
+    assert (np.abs(acc_got.astype(np.float64) - h["acc"]) <= np.abs(np.spacing(h["acc"]))).all()
+    got = (_gather(P, idx_t).cpu().numpy(), _gather(M, idx_t).cpu().numpy(), _gather(V, idx_t).cpu().numpy(),
+           bits_of(_gather(par, idx_t)))
+    ref = oracle.shard_step(h["p"], h["m"], h["v"], h["acc"], "f32", w.param_dtype, global_sq=ref_sq,
+                            global_overflow=False, **hp)
+    compare_step(got, ref, what="accumulated ")
+    if real < S:
+        assert bool((A[real:] == 0).all().item()) and bool((P[real:] == 0).all().item())
+    del P, M, V, A, par
+    torch.cuda.empty_cache()

@@ -12,18 +12,20 @@ in the library's kernels.
     zero_norm_workspace_bytes(n) -> int
     zero_shard_unscale_norm_overflow(grad, inv_loss_scale, sqnorm, overflow, workspace)
     zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp, global_sqnorm, global_overflow)
+    zero_shard_grad_accumulate(acc, grad, inv_loss_scale, first, overflow=None)
     zero_loss_scaler_update(scaler, overflow) -> skip
 """
 import ctypes
 from typing import List, Optional, Sequence, Tuple
 
 from . import _lib as _L
-from ._lib import (ZERO_BF16, ZERO_F16, ZeroShardError, zero_adam_params,  # noqa: F401
+from ._lib import (ZERO_BF16, ZERO_F16, ZERO_F32, ZeroShardError, zero_adam_params,  # noqa: F401
                    zero_fragment, zero_loss_scaler)
 
 __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_bytes",
-           "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_loss_scaler_update",
-           "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZeroShardError", "AdamHyper",
+           "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_shard_grad_accumulate",
+           "zero_loss_scaler_update", "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZERO_F32",
+           "ZeroShardError", "AdamHyper",
            "LossScaler", "dtype_code", "ShardAdam"]
 
 
@@ -66,7 +68,7 @@ def zero_norm_workspace_bytes(n: int) -> int:
 
 
 def dtype_code(t) -> int:
-    """ZERO_F16 / ZERO_BF16 from a torch dtype (or pass the code through)."""
+    """ZERO_F16 / ZERO_BF16 / ZERO_F32 from a torch dtype (or pass the code through)."""
     if isinstance(t, int):
         return t
     import torch
@@ -75,7 +77,9 @@ def dtype_code(t) -> int:
         return ZERO_F16
     if dt == torch.bfloat16:
         return ZERO_BF16
-    raise ValueError(f"unsupported 16-bit dtype {dt}")
+    if dt == torch.float32:
+        return ZERO_F32
+    raise ValueError(f"unsupported gradient/parameter dtype {dt}")
 
 
 def _stream(stream) -> Optional[int]:
@@ -143,6 +147,19 @@ def zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: AdamH
                                            _ptr(param_out), pd, n, ctypes.byref(params), _ptr(global_sqnorm),
                                            _ptr(global_overflow), _stream(stream)),
              "zero_shard_adam_step")
+
+
+def zero_shard_grad_accumulate(acc, grad, inv_loss_scale: float, first: bool, overflow=None,
+                               grad_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """Enqueue acc = (first ? 0 : acc) + grad * inv_loss_scale (fp32 acc, 16-bit
+    grad); overflow (int32 [1] or None) is set to 1 if grad holds an inf/NaN."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    if not isinstance(acc, int) and grad.numel() != n:
+        raise ValueError("acc and grad differ in length")
+    _L.check(_L.lib().zero_shard_grad_accumulate(_ptr(acc), _ptr(grad), gd, n, float(inv_loss_scale),
+                                                 1 if first else 0, _ptr(overflow), _stream(stream)),
+             "zero_shard_grad_accumulate")
 
 
 class LossScaler:

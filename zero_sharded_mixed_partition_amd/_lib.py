@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_ENOSPC, ZERO_EHIP = 0, -1, -2, -3, -4, -5
-ZERO_F16, ZERO_BF16 = 1, 2
+ZERO_F16, ZERO_BF16, ZERO_F32 = 1, 2, 3
 
 c_i32, c_i64, c_dbl, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
 P_i64 = ctypes.POINTER(c_i64)
@@ -43,6 +43,7 @@ SIGNATURES = {
     "zero_shard_unscale_norm_overflow": (c_i32, [c_vp, c_i32, c_i64, c_dbl, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "zero_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                      ctypes.POINTER(zero_adam_params), c_vp, c_vp, c_vp]),
+    "zero_shard_grad_accumulate": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_dbl, c_i32, c_vp, c_vp]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
     "zero_status_string": (ctypes.c_char_p, [c_i32]),
     "zero_last_error": (ctypes.c_char_p, []),

@@ -1,32 +1,36 @@
-// Device part of the C ABI: the two streaming passes of one ZeRO rank's
+// Device part of the C ABI: the streaming passes of one ZeRO rank's
 // mixed-precision Adam step over its shard, for gfx950 (MI355X, CDNA4).
 //
 // What is computed follows the explainer "Data Parallelism Without the
 // Copies" of "ZeRO: Memory Optimizations Toward Training Trillion Parameter
 // Models": "The 16 Bytes per Parameter Audit" and Ch.02 "The Three Stages"
-// (fp16 weight + fp32 master + two fp32 moments per parameter; each rank
-// updates only its own partition).  The update rule itself is bias-corrected
-// Adam (Kingma & Ba 2015) with decoupled weight decay (Loshchilov & Hutter
-// 2019); loss scaling and inf/NaN skipping follow Micikevicius et al. 2018;
-// clipping is global max-norm clipping (Pascanu et al. 2013).
+// (fp16 weight + fp32 master + two fp32 moments per parameter, optionally an
+// fp32 copy of the gradient; each rank updates only its own partition).  The
+// update rule itself is bias-corrected Adam (Kingma & Ba 2015) with decoupled
+// weight decay (Loshchilov & Hutter 2019); loss scaling and inf/NaN skipping
+// follow Micikevicius et al. 2018; clipping is global max-norm clipping
+// (Pascanu et al. 2013).
 //
-// Both passes are HBM-bandwidth bound elementwise streams (no contraction, so
-// no MFMA): threads move whole vectors (16 bytes of fp32, 8 or 16 bytes of
+// Every pass is an HBM-bandwidth bound elementwise stream (no contraction,
+// so no MFMA): threads move whole vectors (16 bytes of fp32, 8 or 16 bytes of
 // 16-bit values), consecutive lanes touch consecutive vectors so every wave64
 // access instruction is one contiguous run, and the streams are read once, so
 // loads and stores are marked non-temporal.
 //
-//  pass 1  sqnorm_partials + sqnorm_finalize: reads the 2-byte gradient once
-//          (2 B/element), ORs an exponent-bits inf/NaN test, sums exact fp64
-//          squares per thread in a fixed order, reduces within a wave by
-//          xor-shuffles and across the block's four waves through LDS, then a
-//          one-block kernel combines the block partials in a fixed order.
-//          Only the first block touches the ragged remainder.
-//  pass 2  adam_update: 28 B/element (2 grad + 4 master + 4 m + 4 v read,
-//          4 + 4 + 4 written back, 2 param written).  One wave64 per
-//          workgroup, lane l owning 4 consecutive elements, so each access
-//          instruction is one contiguous, fully used run of cache lines; the
-//          number of resident waves per CU is capped (see kAdamLdsReserve).
+//  sqnorm_partials + sqnorm_finalize: reads the gradient once (2 B/element,
+//          4 for an fp32 gradient), ORs an exponent-bits inf/NaN test, sums
+//          exact fp64 squares per thread in a fixed order, reduces within a
+//          wave by xor-shuffles and across the block's four waves through
+//          LDS, then a one-block kernel combines the block partials in a
+//          fixed order.  Only the first block touches the ragged remainder.
+//  adam_update: 28 B/element (2 grad + 4 master + 4 m + 4 v read, 4 + 4 + 4
+//          written back, 2 param written; 30 with an fp32 gradient).  One
+//          wave64 per workgroup, lane l owning 4 consecutive elements, so
+//          each access instruction is one contiguous, fully used run of
+//          cache lines; the number of resident waves per CU is capped.
+//  grad_accumulate: acc = (first ? 0 : acc) + g * inv_scale into the fp32
+//          gradient copy, 10 B/element (6 for the first micro-batch), same
+//          launch shape as adam_update.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -44,24 +48,50 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;              // four wave64s
 constexpr int kWaves = kBlock / 64;
-// norm pass: 512 blocks of 256 threads (2 per CU), each step of the
-// grid-stride loop reads a 16 KiB chunk per block; chosen by measurement on
-// MI355X (~7.1 TB/s on a 2 GB gradient shard)
+// norm pass: at most 512 blocks of 256 threads (2 per CU); each step of the
+// grid-stride loop reads a 16 KiB chunk per block.  Chosen by measurement on
+// MI355X (~7.1 TB/s on a 2 GB gradient shard).
 constexpr int kNormMaxBlocks = 512;
-constexpr int kNormUnroll = 4;                          // 16-byte loads in flight per thread
+constexpr int kNormUnroll = 4;                                  // 16-byte loads in flight per thread
 constexpr int64_t kNormChunk = (int64_t)kBlock * kNormUnroll;   // vectors per block per step
-// fused update: one wave64 per workgroup, 4 consecutive elements per lane
-constexpr int kAdamThreads = 64;
-constexpr int kAdamTask = 4 * kAdamThreads;             // elements per workgroup per task
+// elementwise passes: one wave64 per workgroup, 4 consecutive elements per lane
+constexpr int kEwThreads = 64;
+constexpr int kEwTask = 4 * kEwThreads;                         // elements per workgroup per task
 // Occupancy cap.  With eight streams in flight HBM sustains more bytes per
 // second when fewer waves compete for DRAM rows: 12 KiB of LDS per
 // workgroup leaves room for 13 resident one-wave workgroups per CU (160 KiB
 // of LDS per CU on gfx950).  Chosen by measurement on MI355X over 0-32 KiB
 // (0 KiB: ~75% of HBM peak; 12 KiB: ~82%; 32 KiB: ~55%).
 constexpr size_t kAdamLdsReserve = 12 * 1024;
-constexpr int64_t kAdamMaxGrid = (int64_t(1) << 26) - 1;   // grid * 64 work-items < 2^32
+constexpr size_t kAccumLdsReserve = 12 * 1024;
+constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
 
-// ---------------------------------------------------------------- 16-bit helpers
+// ---------------------------------------------------------------- gradient formats
+
+// Per gradient format: values per 16-byte vector, and the exponent-field test.
+// For a 32-bit word w, (w & mask) + carry sets bit 15 (low 16-bit half) or
+// bit 31 (high half, or the whole fp32 value) exactly when that value's
+// exponent field is all ones, i.e. it is inf or NaN; no carry crosses into
+// the neighbouring field.  OR-accumulating these words and testing
+// kNonfiniteBits at the end is an exact inf/NaN test.
+template <int DT>
+struct GradFmt;
+template <>
+struct GradFmt<ZERO_F16> {
+    static constexpr int per_vec = 8;
+    static constexpr uint32_t mask = 0x7C007C00u, carry = 0x04000400u;
+};
+template <>
+struct GradFmt<ZERO_BF16> {
+    static constexpr int per_vec = 8;
+    static constexpr uint32_t mask = 0x7F807F80u, carry = 0x00800080u;
+};
+template <>
+struct GradFmt<ZERO_F32> {
+    static constexpr int per_vec = 4;
+    static constexpr uint32_t mask = 0x7F800000u, carry = 0x00800000u;
+};
+constexpr uint32_t kNonfiniteBits = 0x80008000u;
 
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -96,6 +126,32 @@ __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontempora
 template <typename T>
 __device__ __forceinline__ void st_stream(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
+// the 4 gradient values of element group q (elements 4q .. 4q+3)
+template <int DT>
+__device__ __forceinline__ void load_grad4(const void* G, int64_t q, float g[4]) {
+    if constexpr (DT == ZERO_F32) {
+        const f32x4 v = ld_stream(static_cast<const f32x4*>(G) + q);
+        g[0] = v[0];
+        g[1] = v[1];
+        g[2] = v[2];
+        g[3] = v[3];
+    } else {
+        const u32x2 w = ld_stream(static_cast<const u32x2*>(G) + q);
+        unpack2<DT>(w[0], g[0], g[1]);
+        unpack2<DT>(w[1], g[2], g[3]);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_grad1(const void* G, int64_t e) {
+    if constexpr (DT == ZERO_F32) {
+        return static_cast<const float*>(G)[e];
+    } else {
+        const uint32_t h = static_cast<const uint16_t*>(G)[e];
+        return DT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+    }
+}
+
 // ---------------------------------------------------------------- block reduction
 
 __device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad, double* s_sq, uint32_t* s_bad) {
@@ -121,29 +177,23 @@ __device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad, double*
     }
 }
 
-// ---------------------------------------------------------------- pass 1
-
-// Per 32-bit word of two 16-bit values: (w & E) + C sets bit 15 (bit 31) iff
-// the low (high) half has an all-ones exponent field, i.e. is inf or NaN;
-// no carry crosses from the low half into the high half.  OR-accumulating
-// these words and testing kNonfiniteBits at the end is an exact inf/NaN test.
-template <int DT>
-struct Exp16 {
-    static constexpr uint32_t mask2 = DT == ZERO_F16 ? 0x7C007C00u : 0x7F807F80u;
-    static constexpr uint32_t carry2 = DT == ZERO_F16 ? 0x04000400u : 0x00800080u;
-};
-constexpr uint32_t kNonfiniteBits = 0x80008000u;
+// ---------------------------------------------------------------- norm pass
 
 template <int DT>
 __device__ __forceinline__ void accumulate_vec(u32x4 q, double& acc, uint32_t& bad) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        float lo, hi;
-        unpack2<DT>(q[k], lo, hi);
-        bad |= (q[k] & Exp16<DT>::mask2) + Exp16<DT>::carry2;
-        const double a = (double)lo, b = (double)hi;   // exact; squares exact in fp64
-        acc = fma(a, a, acc);
-        acc = fma(b, b, acc);
+        bad |= (q[k] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+        if constexpr (DT == ZERO_F32) {
+            const double a = (double)__uint_as_float(q[k]);   // exact; square exact in fp64
+            acc = fma(a, a, acc);
+        } else {
+            float lo, hi;
+            unpack2<DT>(q[k], lo, hi);
+            const double a = (double)lo, b = (double)hi;
+            acc = fma(a, a, acc);
+            acc = fma(b, b, acc);
+        }
     }
 }
 
@@ -153,7 +203,7 @@ __device__ __forceinline__ void accumulate_vec(u32x4 q, double& acc, uint32_t& b
 // order (and the result) is the same on every run.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restrict__ g, int64_t nvec,
-                                                          const uint16_t* __restrict__ tail, int tail_n,
+                                                          const void* __restrict__ tail, int tail_n,
                                                           double* __restrict__ part_sq,
                                                           uint32_t* __restrict__ part_bad) {
     __shared__ double s_sq[kWaves];
@@ -170,15 +220,16 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restric
         for (int u = 0; u < kNormUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
     }
     if (blockIdx.x == 0) {
-        // fewer than kNormChunk vectors left over, then fewer than 8 elements
+        // fewer than kNormChunk vectors left over, then less than one vector
         for (int64_t i = nchunks * kNormChunk + threadIdx.x; i < nvec; i += kBlock)
             accumulate_vec<DT>(ld_stream(g + i), acc, bad);
         if (threadIdx.x == 0) {
             for (int k = 0; k < tail_n; ++k) {
-                const uint32_t h = tail[k];
-                const float x = DT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
-                bad |= (h & Exp16<DT>::mask2) + Exp16<DT>::carry2;
-                const double a = (double)x;
+                uint32_t w;
+                if constexpr (DT == ZERO_F32) w = static_cast<const uint32_t*>(tail)[k];
+                else w = static_cast<const uint16_t*>(tail)[k];
+                bad |= (w & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                const double a = (double)load_grad1<DT>(tail, k);
                 acc = fma(a, a, acc);
             }
         }
@@ -211,14 +262,15 @@ __global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restri
     }
 }
 
-int norm_blocks(int64_t n) {
-    int64_t b = (n / 8) / kNormChunk;      // one block per full chunk, at most kNormMaxBlocks
+// blocks for a gradient of nvec 16-byte vectors: one per full chunk, at most kNormMaxBlocks
+int norm_blocks(int64_t nvec) {
+    int64_t b = nvec / kNormChunk;
     if (b < 1) b = 1;
     if (b > kNormMaxBlocks) b = kNormMaxBlocks;
     return (int)b;
 }
 
-// ---------------------------------------------------------------- pass 2
+// ---------------------------------------------------------------- fused AdamW
 
 struct AdamCoef {
     float beta1, omb1, beta2, omb2;   // beta, 1 - beta (each rounded once from double)
@@ -241,12 +293,11 @@ __device__ __forceinline__ void adam_elem(const AdamCoef& c, float gscale, float
 }
 
 template <int GDT, int PDT, bool WRITE_P>
-__global__ __launch_bounds__(kAdamThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
-                                                            float* __restrict__ V,
-                                                            const uint16_t* __restrict__ G,
-                                                            uint16_t* __restrict__ Pout, int64_t n, AdamCoef c,
-                                                            const double* __restrict__ d_sq,
-                                                            const int32_t* __restrict__ d_ovf) {
+__global__ __launch_bounds__(kEwThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
+                                                          float* __restrict__ V, const void* __restrict__ G,
+                                                          uint16_t* __restrict__ Pout, int64_t n, AdamCoef c,
+                                                          const double* __restrict__ d_sq,
+                                                          const int32_t* __restrict__ d_ovf) {
     // Dynamic LDS reserved by the launcher only to cap how many of these
     // workgroups (one wave each) are resident per CU; it is never read.
     extern __shared__ float occupancy_pad[];
@@ -260,21 +311,19 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update(float* __restrict__ 
         gscale = (float)(c.inv_scale * coef);
     }
     const int lane = threadIdx.x;
-    const int64_t ntasks = (n + kAdamTask - 1) / kAdamTask;
+    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
     for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
         // lane owns elements [e0, e0 + 4): every access instruction of the wave
         // covers one contiguous run (1 KiB per fp32 stream, 512 B per 16-bit one)
-        const int64_t e0 = t * kAdamTask + 4 * lane;
+        const int64_t e0 = t * kEwTask + 4 * lane;
         if (e0 + 4 <= n) {
             const int64_t q = e0 >> 2;
             f32x4* p4 = reinterpret_cast<f32x4*>(P) + q;
             f32x4* m4 = reinterpret_cast<f32x4*>(M) + q;
             f32x4* v4 = reinterpret_cast<f32x4*>(V) + q;
             f32x4 p = ld_stream(p4), m = ld_stream(m4), v = ld_stream(v4);
-            const u32x2 gq = ld_stream(reinterpret_cast<const u32x2*>(G) + q);
             float g[4];
-            unpack2<GDT>(gq[0], g[0], g[1]);
-            unpack2<GDT>(gq[1], g[2], g[3]);
+            load_grad4<GDT>(G, q, g);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 float pk = p[k], mk = m[k], vk = v[k];
@@ -295,10 +344,8 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update(float* __restrict__ 
         } else if (e0 < n) {
             // ragged tail: the last 1-3 elements, scalar accesses
             for (int64_t e = e0; e < n; ++e) {
-                const uint32_t h = G[e];
-                const float graw = GDT == ZERO_F16 ? f16_to_f32(h) : bf16_to_f32(h);
                 float p = P[e], m = M[e], v = V[e];
-                adam_elem(c, gscale, graw, p, m, v);
+                adam_elem(c, gscale, load_grad1<GDT>(G, e), p, m, v);
                 P[e] = p;
                 M[e] = m;
                 V[e] = v;
@@ -306,6 +353,50 @@ __global__ __launch_bounds__(kAdamThreads) void adam_update(float* __restrict__ 
             }
         }
     }
+    if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
+}
+
+// ---------------------------------------------------------------- gradient accumulation
+
+template <int DT, bool FIRST>
+__global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict__ A, const void* __restrict__ G,
+                                                              int64_t n, float inv,
+                                                              int32_t* __restrict__ d_ovf) {
+    extern __shared__ float occupancy_pad[];   // occupancy cap only, never read
+    uint32_t bad = 0;
+    const int lane = threadIdx.x;
+    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
+    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
+        const int64_t e0 = t * kEwTask + 4 * lane;
+        if (e0 + 4 <= n) {
+            const int64_t q = e0 >> 2;
+            const u32x2 w = ld_stream(static_cast<const u32x2*>(G) + q);
+            bad |= (w[0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+            bad |= (w[1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+            float g[4];
+            unpack2<DT>(w[0], g[0], g[1]);
+            unpack2<DT>(w[1], g[2], g[3]);
+            f32x4* a4 = reinterpret_cast<f32x4*>(A) + q;
+            f32x4 a;
+            if constexpr (FIRST) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) a[k] = g[k] * inv;
+            } else {
+                a = ld_stream(a4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) a[k] = fmaf(g[k], inv, a[k]);   // one rounding
+            }
+            st_stream(a, a4);
+        } else if (e0 < n) {
+            for (int64_t e = e0; e < n; ++e) {
+                const uint32_t h = static_cast<const uint16_t*>(G)[e];
+                bad |= (h & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                const float g = load_grad1<DT>(G, e);
+                A[e] = FIRST ? g * inv : fmaf(g, inv, A[e]);
+            }
+        }
+    }
+    if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
     if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
 }
 
@@ -324,11 +415,36 @@ int launch_status(const char* what) {
     return ZERO_OK;
 }
 
+int grad_bytes(int32_t dt) { return dt == ZERO_F32 ? 4 : 2; }
+
+dim3 elementwise_grid(int64_t n) {
+    int64_t ntasks = (n + kEwTask - 1) / kEwTask;
+    if (ntasks > kEwMaxGrid) ntasks = kEwMaxGrid;   // the kernels stride over the rest
+    return dim3((unsigned)ntasks);
+}
+
+template <int DT>
+void launch_norm(int nb, hipStream_t s, const void* grad, int64_t n, double* part_sq, uint32_t* part_bad) {
+    const int64_t nvec = n / GradFmt<DT>::per_vec;
+    const int tail_n = (int)(n - nvec * GradFmt<DT>::per_vec);
+    const void* tail = static_cast<const char*>(grad) + nvec * 16;
+    hipLaunchKernelGGL(sqnorm_partials<DT>, dim3(nb), dim3(kBlock), 0, s, static_cast<const u32x4*>(grad), nvec,
+                       tail, tail_n, part_sq, part_bad);
+}
+
 template <int GDT, int PDT, bool WRITE_P>
 void launch_adam(dim3 grid, hipStream_t s, float* P, float* M, float* V, const void* G, void* Pout,
                  int64_t n, const AdamCoef& c, const double* d_sq, const int32_t* d_ovf) {
-    hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kAdamThreads), kAdamLdsReserve, s, P, M, V,
-                       static_cast<const uint16_t*>(G), static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
+    hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kEwThreads), kAdamLdsReserve, s, P, M, V, G,
+                       static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
+}
+
+template <int GDT>
+void launch_adam_p(dim3 grid, hipStream_t s, bool wp, int pdt, float* P, float* M, float* V, const void* G,
+                   void* Pout, int64_t n, const AdamCoef& c, const double* d_sq, const int32_t* d_ovf) {
+    if (!wp) launch_adam<GDT, ZERO_F16, false>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
+    else if (pdt == ZERO_F16) launch_adam<GDT, ZERO_F16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
+    else launch_adam<GDT, ZERO_BF16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
 }
 
 }  // namespace
@@ -340,7 +456,8 @@ extern "C" {
 
 size_t zero_norm_workspace_bytes(int64_t n) {
     if (n < 0) return 0;
-    const size_t b = (size_t)norm_blocks(n);
+    // sized for the format with the most 16-byte vectors (fp32: 4 per vector)
+    const size_t b = (size_t)norm_blocks((n + 3) / 4);
     return ((b * (sizeof(double) + sizeof(uint32_t))) + 255) & ~(size_t)255;
 }
 
@@ -349,7 +466,8 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
                                      size_t workspace_bytes, void* hip_stream) {
     clear_error();
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
-    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16) return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
+        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
     if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
         return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
     if (d_sqnorm == nullptr || d_overflow == nullptr || d_workspace == nullptr)
@@ -362,19 +480,14 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
     if (workspace_bytes < zero_norm_workspace_bytes(n))
         return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, zero_norm_workspace_bytes(n));
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const int nb = norm_blocks(n);
+    const int64_t per_vec = grad_dtype == ZERO_F32 ? 4 : 8;
+    const int nb = norm_blocks(n / per_vec);
     double* part_sq = static_cast<double*>(d_workspace);
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + nb);
-    const int64_t nvec = n / 8;
-    const int tail_n = (int)(n - nvec * 8);
-    const uint16_t* tail = static_cast<const uint16_t*>(grad) + nvec * 8;
     if (n > 0) {
-        if (grad_dtype == ZERO_F16)
-            hipLaunchKernelGGL(sqnorm_partials<ZERO_F16>, dim3(nb), dim3(kBlock), 0, s,
-                               static_cast<const u32x4*>(grad), nvec, tail, tail_n, part_sq, part_bad);
-        else
-            hipLaunchKernelGGL(sqnorm_partials<ZERO_BF16>, dim3(nb), dim3(kBlock), 0, s,
-                               static_cast<const u32x4*>(grad), nvec, tail, tail_n, part_sq, part_bad);
+        if (grad_dtype == ZERO_F16) launch_norm<ZERO_F16>(nb, s, grad, n, part_sq, part_bad);
+        else if (grad_dtype == ZERO_BF16) launch_norm<ZERO_BF16>(nb, s, grad, n, part_sq, part_bad);
+        else launch_norm<ZERO_F32>(nb, s, grad, n, part_sq, part_bad);
         const int st = launch_status("sqnorm_partials");
         if (st != ZERO_OK) return st;
     }
@@ -389,7 +502,8 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
     clear_error();
     if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
-    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16) return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
+        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
     if (param_out != nullptr && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "unknown param_dtype %d", param_dtype);
     const zero_adam_params& h = *hp;
@@ -413,9 +527,9 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
     if (d_global_sqnorm && ((uintptr_t)d_global_sqnorm & 7u)) return fail(ZERO_EALIGN, "d_global_sqnorm misaligned");
     if (d_global_overflow && ((uintptr_t)d_global_overflow & 3u)) return fail(ZERO_EALIGN, "d_global_overflow misaligned");
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
-    const int64_t b32 = n * 4, b16 = n * 2;
-    if (overlaps(grad, b16, master, b32) || overlaps(grad, b16, exp_avg, b32) ||
-        overlaps(grad, b16, exp_avg_sq, b32) || (param_out && overlaps(grad, b16, param_out, b16)))
+    const int64_t b32 = n * 4, b16 = n * 2, bg = n * grad_bytes(grad_dtype);
+    if (overlaps(grad, bg, master, b32) || overlaps(grad, bg, exp_avg, b32) || overlaps(grad, bg, exp_avg_sq, b32) ||
+        (param_out && overlaps(grad, bg, param_out, b16)))
         return fail(ZERO_EINVAL, "grad aliases an output");
     if (overlaps(master, b32, exp_avg, b32) || overlaps(master, b32, exp_avg_sq, b32) ||
         overlaps(exp_avg, b32, exp_avg_sq, b32) ||
@@ -442,25 +556,49 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
     c.inv_scale = h.inv_loss_scale;
     c.max_norm = clip ? h.max_grad_norm : 0.0;
 
-    int64_t ntasks = (n + kAdamTask - 1) / kAdamTask;
-    if (ntasks > kAdamMaxGrid) ntasks = kAdamMaxGrid;   // the kernel strides over the rest
-    const dim3 grid((unsigned)ntasks);
+    const dim3 grid = elementwise_grid(n);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const bool wp = param_out != nullptr;
-    const int pdt = wp ? param_dtype : ZERO_F16;
-#define ZS_LAUNCH(G, P, W) launch_adam<G, P, W>(grid, s, master, exp_avg, exp_avg_sq, grad, param_out, n, c, \
-                                                 d_global_sqnorm, d_global_overflow)
-    if (grad_dtype == ZERO_F16) {
-        if (!wp) ZS_LAUNCH(ZERO_F16, ZERO_F16, false);
-        else if (pdt == ZERO_F16) ZS_LAUNCH(ZERO_F16, ZERO_F16, true);
-        else ZS_LAUNCH(ZERO_F16, ZERO_BF16, true);
-    } else {
-        if (!wp) ZS_LAUNCH(ZERO_BF16, ZERO_BF16, false);
-        else if (pdt == ZERO_BF16) ZS_LAUNCH(ZERO_BF16, ZERO_BF16, true);
-        else ZS_LAUNCH(ZERO_BF16, ZERO_F16, true);
-    }
-#undef ZS_LAUNCH
+    if (grad_dtype == ZERO_F16)
+        launch_adam_p<ZERO_F16>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
+                                d_global_sqnorm, d_global_overflow);
+    else if (grad_dtype == ZERO_BF16)
+        launch_adam_p<ZERO_BF16>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
+                                 d_global_sqnorm, d_global_overflow);
+    else
+        launch_adam_p<ZERO_F32>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
+                                d_global_sqnorm, d_global_overflow);
     return launch_status("adam_update");
+}
+
+int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
+                               int32_t first, int32_t* d_overflow, void* hip_stream) {
+    clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16 (got %d)", grad_dtype);
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    if (n == 0) return ZERO_OK;
+    if (acc == nullptr || grad == nullptr) return fail(ZERO_EINVAL, "NULL acc or grad");
+    if (!aligned16(acc) || !aligned16(grad)) return fail(ZERO_EALIGN, "acc and grad must be 16-byte aligned");
+    if (d_overflow && ((uintptr_t)d_overflow & 3u)) return fail(ZERO_EALIGN, "d_overflow misaligned");
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    if (overlaps(acc, n * 4, grad, n * 2)) return fail(ZERO_EINVAL, "acc aliases grad");
+    const dim3 grid = elementwise_grid(n);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const float inv = (float)inv_loss_scale;
+#define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), kAccumLdsReserve, s, acc, \
+                                         grad, n, inv, d_overflow)
+    if (grad_dtype == ZERO_F16) {
+        if (first) ZS_ACC(ZERO_F16, true);
+        else ZS_ACC(ZERO_F16, false);
+    } else {
+        if (first) ZS_ACC(ZERO_BF16, true);
+        else ZS_ACC(ZERO_BF16, false);
+    }
+#undef ZS_ACC
+    return launch_status("grad_accumulate");
 }
 
 }  // extern "C"

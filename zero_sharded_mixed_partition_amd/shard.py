@@ -1,6 +1,8 @@
 """ShardAdam: one rank's optimizer shard driven through the C ABI.
 
-A step is: enqueue the unscale/overflow/norm pass on the gradient shard,
+A step is: (optionally, micro-batch by micro-batch, accumulate the 16-bit
+gradients into an fp32 copy), enqueue the unscale/overflow/norm pass on the
+gradient shard (16-bit, or the fp32 copy),
 (in a multi-rank job: all-reduce the two scalars), enqueue the fused AdamW
 pass, then read the 4-byte overflow flag back to update the loss scale and the
 step counter on the host.  The flag read is the step's only device-to-host
@@ -11,8 +13,8 @@ from typing import Callable, Optional
 
 import torch
 
-from . import (AdamHyper, LossScaler, dtype_code, zero_loss_scaler_update, zero_norm_workspace_bytes,
-               zero_shard_adam_step, zero_shard_unscale_norm_overflow)
+from . import (ZERO_F32, AdamHyper, LossScaler, dtype_code, zero_loss_scaler_update, zero_norm_workspace_bytes,
+               zero_shard_adam_step, zero_shard_grad_accumulate, zero_shard_unscale_norm_overflow)
 
 
 class ShardAdam:
@@ -35,14 +37,24 @@ class ShardAdam:
         self._flag_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
         self._flag_ready = torch.cuda.Event()
 
+    def _inv_scale(self, grad: torch.Tensor) -> float:
+        # an fp32 gradient is the accumulation copy, already unscaled
+        return 1.0 if dtype_code(grad) == ZERO_F32 else 1.0 / self.scaler.scale
+
+    def accumulate(self, acc: torch.Tensor, grad: torch.Tensor, first: bool,
+                   overflow: Optional[torch.Tensor] = None) -> None:
+        """Enqueue one micro-batch into the fp32 gradient copy `acc`
+        (acc = (first ? 0 : acc) + grad / loss_scale)."""
+        zero_shard_grad_accumulate(acc, grad, 1.0 / self.scaler.scale, first, overflow)
+
     def unscale_norm(self, grad: torch.Tensor) -> None:
         """Enqueue steps 1-2: self.sqnorm, self.overflow <- this shard's values."""
-        zero_shard_unscale_norm_overflow(grad, 1.0 / self.scaler.scale, self.sqnorm, self.overflow, self.workspace)
+        zero_shard_unscale_norm_overflow(grad, self._inv_scale(grad), self.sqnorm, self.overflow, self.workspace)
 
     def apply(self, grad: torch.Tensor, param_out: Optional[torch.Tensor], global_sqnorm=None,
               global_overflow=None) -> None:
         """Enqueue steps 3-4 for step index t+1 (skipped on device on overflow)."""
-        hp = AdamHyper(step=self.t + 1, inv_loss_scale=1.0 / self.scaler.scale, **self.hyper)
+        hp = AdamHyper(step=self.t + 1, inv_loss_scale=self._inv_scale(grad), **self.hyper)
         zero_shard_adam_step(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out, hp,
                              self.sqnorm if global_sqnorm is None else global_sqnorm,
                              self.overflow if global_overflow is None else global_overflow,
