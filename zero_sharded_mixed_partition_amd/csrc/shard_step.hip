@@ -29,8 +29,8 @@
 //          each access instruction is one contiguous, fully used run of
 //          cache lines; the number of resident waves per CU is capped.
 //  grad_accumulate: acc = (first ? 0 : acc) + g * inv_scale into the fp32
-//          gradient copy, 10 B/element (6 for the first micro-batch), same
-//          launch shape as adam_update.
+//          gradient copy, 10 B/element (6 for the first micro-batch), the
+//          same lane layout as adam_update but with no occupancy cap.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -63,7 +63,8 @@ constexpr int kEwTask = 4 * kEwThreads;                         // elements per 
 // of LDS per CU on gfx950).  Chosen by measurement on MI355X over 0-32 KiB
 // (0 KiB: ~75% of HBM peak; 12 KiB: ~82%; 32 KiB: ~55%).
 constexpr size_t kAdamLdsReserve = 12 * 1024;
-constexpr size_t kAccumLdsReserve = 12 * 1024;
+// The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
+// peak with no reservation against 45-63% with the 12 KiB cap.
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
 
 // ---------------------------------------------------------------- gradient formats
@@ -362,7 +363,6 @@ template <int DT, bool FIRST>
 __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict__ A, const void* __restrict__ G,
                                                               int64_t n, float inv,
                                                               int32_t* __restrict__ d_ovf) {
-    extern __shared__ float occupancy_pad[];   // occupancy cap only, never read
     uint32_t bad = 0;
     const int lane = threadIdx.x;
     const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
@@ -397,7 +397,6 @@ __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict_
         }
     }
     if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
-    if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -588,8 +587,8 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
     const dim3 grid = elementwise_grid(n);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const float inv = (float)inv_loss_scale;
-#define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), kAccumLdsReserve, s, acc, \
-                                         grad, n, inv, d_overflow)
+#define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), 0, s, acc, grad, n, inv, \
+                                         d_overflow)
     if (grad_dtype == ZERO_F16) {
         if (first) ZS_ACC(ZERO_F16, true);
         else ZS_ACC(ZERO_F16, false);
