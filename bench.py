@@ -112,6 +112,63 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24):
                       f"input generation excluded"}
 
 
+def bench_offload(w, args):
+    """The offloaded step: fp32 state in pinned host memory, the 16-bit
+    gradient on the device; per step D2H gradient, host norm + AdamW, H2D
+    parameters.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import zero_sharded_mixed_partition_amd as Z
+    torch.cuda.set_device(0)
+    _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+    begin = w.rank * S
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    host = [torch.empty(S, dtype=torch.float32, pin_memory=True) for _ in range(3)]
+    G = torch.empty(S, dtype=tdt[w.grad_dtype], device="cuda")
+    blk = 16 * W.CHUNK
+    for lo in range(0, S, blk):
+        cnt = min(blk, S - lo)
+        for name, dst in zip(("master", "exp_avg", "exp_avg_sq"), host):
+            dst[lo:lo + cnt].copy_(torch.from_numpy(W.fill(w, name, begin + lo, cnt)))
+        g = W.fill(w, "grad", begin + lo, cnt, step=w.step)
+        G[lo:lo + cnt].copy_(torch.from_numpy(g.view(np.int16)).view(G.dtype))
+        print(f"# prepared {lo + cnt}/{S} elements", file=sys.stderr, flush=True)
+    par = torch.empty(S, dtype=tdt[w.param_dtype], device="cuda")
+    opt = Z.OffloadShardAdam(*host, grad_dtype=tdt[w.grad_dtype], param_dtype=tdt[w.param_dtype], lr=w.lr,
+                             beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                             max_grad_norm=w.max_grad_norm,
+                             scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0
+                                     else Z.LossScaler.static(1.0)), applied_steps=w.step - 1)
+    for _ in range(args.warmup):
+        opt.step(G, par)
+    torch.cuda.synchronize()
+    phases = {"norm": [], "pipeline": []}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        opt.step(G, par)
+        for k, v in opt.last_times.items():
+            phases[k].append(v)
+        print("# step done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    avg = {k: sum(v) / len(v) * 1e3 for k, v in phases.items()}
+    pcie_bytes = 2 * S
+    out = {
+        "metric": METRIC, "value": S / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "shard_params": S, "path": "CPU offload (fp32 state in pinned host memory)",
+                   "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "host_threads": os.cpu_count()},
+        "offload": {"phase_ms": avg, "chunk": opt.chunk, "norm_on": "device",
+                    "pcie_gbps_each_way": pcie_bytes / (avg["pipeline"] * 1e-3) / 1e9,
+                    "host_state_gbps": 24 * S / (avg["pipeline"] * 1e-3) / 1e9},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +179,8 @@ def main():
     ap.add_argument("--accum", type=int, default=0,
                     help="micro-batches accumulated into an fp32 gradient copy per step (0: step the 16-bit "
                          "gradient directly)")
+    ap.add_argument("--offload", action="store_true",
+                    help="keep the fp32 state in pinned host memory and step on host cores (CPU offload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -131,6 +190,9 @@ def main():
 
     import workloads as W
     w = W.get(args.workload)
+
+    if args.offload:
+        return bench_offload(w, args)
 
     cpu = None
     if not args.no_cpu_baseline:

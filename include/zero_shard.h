@@ -204,6 +204,34 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
                                void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * The same step on host cores, for optimizer states kept in host memory (the
+ * CPU-offload lineage: explainer, Legacy, "The trillion-parameter claim";
+ * glossary description, CPU offloading).  All pointers are HOST pointers
+ * (pinned or pageable); the calls are synchronous and return when done.
+ * They compute what the device entry points compute, from the same per-step
+ * coefficients, in float32 with float64 norm partials:
+ *
+ * zero_cpu_shard_unscale_norm_overflow: *sqnorm = sum (grad * inv)^2 over
+ *   [0, n), summed in float64 per 65536-element chunk and then in chunk
+ *   order, so the result is identical for any thread count; *overflow = 1 if
+ *   any element is inf/NaN.  grad_dtype ZERO_F16, ZERO_BF16 or ZERO_F32.
+ * zero_cpu_shard_adam_step: the fused AdamW update of master/exp_avg/
+ *   exp_avg_sq in place and the 16-bit parameter writeback (param_out may be
+ *   NULL), with the data-parallel-reduced norm and flag passed by value;
+ *   global_overflow != 0 leaves every buffer untouched.
+ * nthreads <= 0 uses every hardware thread.  Buffers must not overlap.
+ * Errors: ZERO_EINVAL, ZERO_ERANGE.
+ * ------------------------------------------------------------------------- */
+int zero_cpu_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64_t n,
+                                         double inv_loss_scale, double* sqnorm, int32_t* overflow,
+                                         int32_t nthreads);
+
+int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                             int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                             const zero_adam_params* hp, double global_sqnorm,
+                             int32_t global_overflow, int32_t nthreads);
+
+/* ---------------------------------------------------------------------------
  * Step 2 (scalar, host): dynamic loss scale update after a step.
  * On overflow: *skip_out = 1, scale = max(scale*backoff, min_scale),
  * good_steps = 0.  Otherwise *skip_out = 0, good_steps += 1 and, when it

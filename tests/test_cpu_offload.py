@@ -1,0 +1,112 @@
+"""The host-memory (CPU offload) shard step through the C ABI against the
+oracle.  These run on the CPU: the entry points take host pointers."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+import zero_sharded_mixed_partition_amd as Z
+from zero_sharded_mixed_partition_amd import _lib as L
+
+from parity import check_norm, compare_step
+
+CODE = {"f16": L.ZERO_F16, "bf16": L.ZERO_BF16, "f32": L.ZERO_F32}
+SIZES = [1, 3, 7, 8, 2047, 2048, 2049, 65536, 65537, 200_003]
+
+
+def _inputs(fmt_g, n, begin):
+    w = W.GPT2_SMALL if fmt_g != "bf16" else W.LLAMA_7B
+    p, m, v, g = W.shard_inputs(w, begin, n)
+    if fmt_g == "f32":
+        g = (W.fill(w, "master", begin + 7, n) * np.float32(1e-2)).astype(np.float32)
+    return w, p, m, v, g
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("gfmt,pfmt", [("f16", "f16"), ("bf16", "bf16"), ("f32", "bf16"), ("f16", "bf16"),
+                                       ("bf16", None)])
+def test_cpu_step_matches_oracle(n, gfmt, pfmt):
+    w, p, m, v, g = _inputs(gfmt, n, 12345 + n)
+    inv = 1.0 if gfmt == "f32" else 1.0 / w.loss_scale
+    sq, ovf = Z.zero_cpu_shard_unscale_norm_overflow(g, inv, grad_dtype=CODE[gfmt])
+    ref_sq, ref_ovf = oracle.shard_sqnorm_overflow(g, gfmt, inv)
+    assert ovf == ref_ovf is False
+    check_norm(sq, ref_sq)
+    P, M, V = p.copy(), m.copy(), v.copy()
+    par = np.zeros(n, np.uint16) if pfmt else None
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.05, max_grad_norm=0.01,
+              step=13, inv_loss_scale=inv)
+    Z.zero_cpu_shard_adam_step(P, M, V, g, par, Z.AdamHyper(**hp), sq, ovf, grad_dtype=CODE[gfmt],
+                               param_dtype=CODE[pfmt] if pfmt else None)
+    ref = oracle.shard_step(p, m, v, g, gfmt, pfmt, global_sq=ref_sq, global_overflow=False, **hp)
+    compare_step((P, M, V, par), ref)
+
+
+def test_thread_count_does_not_change_results():
+    w, p, m, v, g = _inputs("bf16", 1_000_003, 5)
+    outs = []
+    for t in (1, 3, 8):
+        sq, ovf = Z.zero_cpu_shard_unscale_norm_overflow(g, 1.0, grad_dtype=L.ZERO_BF16, nthreads=t)
+        P, M, V = p.copy(), m.copy(), v.copy()
+        par = np.zeros(g.size, np.uint16)
+        Z.zero_cpu_shard_adam_step(P, M, V, g, par, Z.AdamHyper(max_grad_norm=1.0, step=3), sq, ovf,
+                                   grad_dtype=L.ZERO_BF16, param_dtype=L.ZERO_BF16, nthreads=t)
+        outs.append((sq, P.view(np.uint32), M.view(np.uint32), V.view(np.uint32), par))
+    for o in outs[1:]:
+        assert o[0] == outs[0][0]
+        for a, b in zip(o[1:], outs[0][1:]):
+            assert (a == b).all()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "f32"])
+def test_overflow_and_skip(fmt):
+    w, p, m, v, g = _inputs(fmt, 70_001, 99)
+    for pos in (0, 35_000, 70_000):
+        h = g.copy()
+        if fmt == "f32":
+            h[pos] = np.inf
+        else:
+            h[pos] = W.POS_INF_BITS[fmt]
+        sq, ovf = Z.zero_cpu_shard_unscale_norm_overflow(h, 1.0, grad_dtype=CODE[fmt])
+        assert ovf and math.isinf(sq)
+        P = p.copy()
+        par = np.full(h.size, 0x1234, np.uint16)
+        Z.zero_cpu_shard_adam_step(P, m.copy(), v.copy(), h, par, Z.AdamHyper(max_grad_norm=1.0), sq, ovf,
+                                   grad_dtype=CODE[fmt], param_dtype=L.ZERO_F16)
+        assert (P.view(np.uint32) == p.view(np.uint32)).all() and (par == 0x1234).all()
+
+
+def test_every_fp16_pattern_decodes_and_rounds():
+    """All 65536 fp16 patterns through the host norm (decode) and every
+    finite fp16 value of a master through the fp16 writeback (encode)."""
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = allp[~oracle.is_nonfinite16(allp, "f16")]
+    sq, ovf = Z.zero_cpu_shard_unscale_norm_overflow(fin, 1.0, grad_dtype=L.ZERO_F16)
+    ref, _ = oracle.shard_sqnorm_overflow(fin, "f16", 1.0)
+    assert not ovf and abs(sq - ref) <= 1e-15 * ref
+    # writeback: with lr = 0 the update leaves the master unchanged, so the
+    # parameter copy is the rounding of the given fp32 values
+    rng = np.random.default_rng(0)
+    x = np.concatenate([oracle.decode16(fin, "f16").astype(np.float32),
+                        (rng.standard_normal(100_000) * np.exp(rng.uniform(-20, 12, 100_000))).astype(np.float32)])
+    for pfmt in ("f16", "bf16"):
+        par = np.zeros(x.size, np.uint16)
+        z = np.zeros(x.size, np.float32)
+        Z.zero_cpu_shard_adam_step(x.copy(), z.copy(), z.copy(), z.copy(), par, Z.AdamHyper(lr=0.0), 0.0, False,
+                                   grad_dtype=L.ZERO_F32, param_dtype=CODE[pfmt])
+        assert (par == oracle.encode16_rne(x, pfmt)).all()
+
+
+def test_cpu_entry_points_reject_bad_arguments():
+    a = np.zeros(16, np.float32)
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_cpu_shard_unscale_norm_overflow(a, 0.0)
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_cpu_shard_unscale_norm_overflow(a, 1.0, grad_dtype=9)
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_cpu_shard_adam_step(a, a, a.copy(), np.zeros(16, np.float32), None, Z.AdamHyper(), 0.0, False)
+    with pytest.raises(Z.ZeroShardError):
+        Z.zero_cpu_shard_adam_step(a, a.copy(), a.copy(), a.copy(), None, Z.AdamHyper(step=0), 0.0, False)
+    assert Z.zero_cpu_shard_unscale_norm_overflow(np.zeros(0, np.float32), 1.0) == (0.0, False)

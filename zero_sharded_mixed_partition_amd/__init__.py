@@ -13,6 +13,8 @@ in the library's kernels.
     zero_shard_unscale_norm_overflow(grad, inv_loss_scale, sqnorm, overflow, workspace)
     zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp, global_sqnorm, global_overflow)
     zero_shard_grad_accumulate(acc, grad, inv_loss_scale, first, overflow=None)
+    zero_cpu_shard_unscale_norm_overflow(grad, inv_loss_scale) -> (sq, overflow)      host memory
+    zero_cpu_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp, sq, overflow)  host memory
     zero_loss_scaler_update(scaler, overflow) -> skip
 """
 import ctypes
@@ -24,9 +26,10 @@ from ._lib import (ZERO_BF16, ZERO_F16, ZERO_F32, ZeroShardError, zero_adam_para
 
 __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_bytes",
            "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_shard_grad_accumulate",
+           "zero_cpu_shard_unscale_norm_overflow", "zero_cpu_shard_adam_step",
            "zero_loss_scaler_update", "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZERO_F32",
            "ZeroShardError", "AdamHyper",
-           "LossScaler", "dtype_code", "ShardAdam"]
+           "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam"]
 
 
 def zero_abi_version() -> int:
@@ -162,6 +165,66 @@ def zero_shard_grad_accumulate(acc, grad, inv_loss_scale: float, first: bool, ov
              "zero_shard_grad_accumulate")
 
 
+# ---------------------------------------------------------------- host-memory (offload) entry points
+
+def _host_ptr(a) -> Optional[int]:
+    """Address of a C-contiguous numpy array or CPU torch tensor."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "ctypes"):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("C-contiguous host array expected")
+        return a.ctypes.data
+    if a.is_cuda or not a.is_contiguous():
+        raise ValueError("contiguous host tensor expected")
+    return a.data_ptr()
+
+
+def _host_code(a, code: Optional[int]) -> int:
+    if code is not None:
+        return code
+    if hasattr(a, "ctypes"):
+        import numpy as np
+        if a.dtype == np.float16:
+            return ZERO_F16
+        if a.dtype == np.float32:
+            return ZERO_F32
+        raise ValueError("pass grad_dtype / param_dtype for raw 16-bit patterns")
+    return dtype_code(a)
+
+
+def zero_cpu_shard_unscale_norm_overflow(grad, inv_loss_scale: float, grad_dtype: Optional[int] = None,
+                                         n: Optional[int] = None, nthreads: int = 0):
+    """Host-memory norm pass; returns (sum of squares, overflow)."""
+    gd = _host_code(grad, grad_dtype)
+    n = (grad.size if hasattr(grad, "ctypes") else grad.numel()) if n is None else n
+    sq, ovf = ctypes.c_double(), ctypes.c_int32()
+    _L.check(_L.lib().zero_cpu_shard_unscale_norm_overflow(_host_ptr(grad), gd, n, float(inv_loss_scale),
+                                                           ctypes.byref(sq), ctypes.byref(ovf), int(nthreads)),
+             "zero_cpu_shard_unscale_norm_overflow")
+    return sq.value, bool(ovf.value)
+
+
+def zero_cpu_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: AdamHyper, global_sqnorm: float,
+                             global_overflow: bool, grad_dtype: Optional[int] = None,
+                             param_dtype: Optional[int] = None, n: Optional[int] = None, nthreads: int = 0) -> None:
+    """Host-memory fused AdamW step (synchronous)."""
+    gd = _host_code(grad, grad_dtype)
+    pd = 0 if param_out is None else _host_code(param_out, param_dtype)
+    size = lambda a: a.size if hasattr(a, "ctypes") else a.numel()  # noqa: E731
+    n = size(master) if n is None else n
+    for a in (exp_avg, exp_avg_sq, grad) + (() if param_out is None else (param_out,)):
+        if not isinstance(a, int) and size(a) != n:
+            raise ValueError("shard arrays differ in length")
+    params = hp.c()
+    _L.check(_L.lib().zero_cpu_shard_adam_step(_host_ptr(master), _host_ptr(exp_avg), _host_ptr(exp_avg_sq),
+                                               _host_ptr(grad), gd, _host_ptr(param_out), pd, n, ctypes.byref(params),
+                                               float(global_sqnorm), 1 if global_overflow else 0, int(nthreads)),
+             "zero_cpu_shard_adam_step")
+
+
 class LossScaler:
     """Host-side dynamic loss scale (C struct zero_loss_scaler)."""
 
@@ -191,3 +254,4 @@ def zero_loss_scaler_update(scaler: LossScaler, overflow: bool) -> bool:
 
 
 from .shard import ShardAdam  # noqa: E402
+from .offload import OffloadShardAdam  # noqa: E402

@@ -16,9 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libzero_shard.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["host.cpp", "shard_step.hip"]
+HOST_SOURCES = ["host.cpp", "cpu_step.cpp"]      # host C++ only (built by the host compiler)
+DEVICE_SOURCES = ["shard_step.hip"]               # HIP: host launchers + gfx950 kernels
+SOURCES = HOST_SOURCES + DEVICE_SOURCES
 ARCH = "gfx950"
 
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fno-math-errno", "-Wall"]
 # Packed fp32 VALU forms are disabled: the compiler emits plain fp32 ops.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -27,27 +30,44 @@ def hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose: bool = False, out_path: str = LIB_PATH, extra_flags=()) -> str:
-    """Compile the library; returns its path.  Raises CalledProcessError."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(suffix=".so", dir=os.path.dirname(out_path))
-    os.close(fd)
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
-           *DEVICE_FLAGS, *extra_flags, *srcs, "-o", tmp]
+def host_cxx() -> str:
+    return os.environ.get("HOST_CXX", "/opt/rocm/bin/amdclang++")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise subprocess.CalledProcessError(res.returncode, cmd, res.stdout, res.stderr)
-        if verbose and res.stderr.strip():
-            sys.stderr.write(res.stderr)
-        os.replace(tmp, out_path)
-    finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise subprocess.CalledProcessError(res.returncode, cmd, res.stdout, res.stderr)
+    if verbose and res.stderr.strip():
+        sys.stderr.write("\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l) + "\n")
+
+
+def build(verbose: bool = False, out_path: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile the library; returns its path.  Raises CalledProcessError."""
+    inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    with tempfile.TemporaryDirectory() as tmpdir:
+        objs = []
+        for src in HOST_SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            _run([host_cxx(), "-x", "c++", *COMMON_FLAGS, "-pthread", *inc, *extra_flags, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        for src in DEVICE_SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            _run([hipcc(), f"--offload-arch={ARCH}", *COMMON_FLAGS, "-Wno-unused-command-line-argument", *inc,
+                  *DEVICE_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        fd, tmp = tempfile.mkstemp(suffix=".so", dir=os.path.dirname(out_path))
+        os.close(fd)
+        try:
+            _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
+            os.replace(tmp, out_path)
+        finally:
+            if os.path.exists(tmp):
+                os.unlink(tmp)
     return out_path
 
 

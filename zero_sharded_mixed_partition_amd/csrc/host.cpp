@@ -8,6 +8,7 @@
 #include "zero_shard.h"
 #include "common.h"
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -27,6 +28,40 @@ int fail(int status, const char* fmt, ...) {
 }
 
 void clear_error() { g_last_error.clear(); }
+
+int prepare_adam(const zero_adam_params* hp, StepCoef* c) {
+    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
+    const zero_adam_params& h = *hp;
+    if (!(h.lr >= 0.0) || !std::isfinite(h.lr)) return fail(ZERO_EINVAL, "lr must be finite and >= 0");
+    if (!(h.beta1 >= 0.0 && h.beta1 < 1.0) || !(h.beta2 >= 0.0 && h.beta2 < 1.0))
+        return fail(ZERO_EINVAL, "betas must lie in [0, 1)");
+    if (!(h.eps >= 0.0) || !std::isfinite(h.eps)) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
+    if (!(h.weight_decay >= 0.0) || !std::isfinite(h.weight_decay))
+        return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
+    if (h.step < 1) return fail(ZERO_EINVAL, "step (1-based index of the step applied) must be >= 1");
+    if (!(h.inv_loss_scale > 0.0) || !std::isfinite(h.inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    const bool clip = h.max_grad_norm > 0.0;
+    if (clip && !std::isfinite(h.max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm must be finite");
+    // bias corrections of the step being applied (Adam, 1-based t)
+    const double t = (double)h.step;
+    const double bc1 = 1.0 - std::pow(h.beta1, t);
+    const double bc2 = 1.0 - std::pow(h.beta2, t);
+    if (!(bc1 > 0.0) || !(bc2 > 0.0)) return fail(ZERO_ERANGE, "bias correction underflows to 0");
+    c->beta1 = (float)h.beta1;
+    c->omb1 = (float)(1.0 - h.beta1);
+    c->beta2 = (float)h.beta2;
+    c->omb2 = (float)(1.0 - h.beta2);
+    c->step_size = (float)(h.lr / bc1);
+    c->rsqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+    c->eps = (float)h.eps;
+    c->decay = (float)(1.0 - h.lr * h.weight_decay);
+    c->gscale_fixed = (float)h.inv_loss_scale;
+    c->clip = clip ? 1 : 0;
+    c->inv_scale = h.inv_loss_scale;
+    c->max_norm = clip ? h.max_grad_norm : 0.0;
+    return ZERO_OK;
+}
 
 namespace {
 

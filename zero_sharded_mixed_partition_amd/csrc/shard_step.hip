@@ -273,18 +273,7 @@ int norm_blocks(int64_t nvec) {
 
 // ---------------------------------------------------------------- fused AdamW
 
-struct AdamCoef {
-    float beta1, omb1, beta2, omb2;   // beta, 1 - beta (each rounded once from double)
-    float step_size;                  // lr / (1 - beta1^t)
-    float rsqrt_bc2;                  // 1 / sqrt(1 - beta2^t)
-    float eps;
-    float decay;                      // 1 - lr * wd
-    float gscale_fixed;               // float(inv_scale) when clipping is off
-    int clip;
-    double inv_scale, max_norm;
-};
-
-__device__ __forceinline__ void adam_elem(const AdamCoef& c, float gscale, float graw, float& p, float& m,
+__device__ __forceinline__ void adam_elem(const StepCoef& c, float gscale, float graw, float& p, float& m,
                                           float& v) {
     const float g = graw * gscale;
     m = fmaf(c.beta1, m, c.omb1 * g);
@@ -296,7 +285,7 @@ __device__ __forceinline__ void adam_elem(const AdamCoef& c, float gscale, float
 template <int GDT, int PDT, bool WRITE_P>
 __global__ __launch_bounds__(kEwThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
                                                           float* __restrict__ V, const void* __restrict__ G,
-                                                          uint16_t* __restrict__ Pout, int64_t n, AdamCoef c,
+                                                          uint16_t* __restrict__ Pout, int64_t n, StepCoef c,
                                                           const double* __restrict__ d_sq,
                                                           const int32_t* __restrict__ d_ovf) {
     // Dynamic LDS reserved by the launcher only to cap how many of these
@@ -433,14 +422,14 @@ void launch_norm(int nb, hipStream_t s, const void* grad, int64_t n, double* par
 
 template <int GDT, int PDT, bool WRITE_P>
 void launch_adam(dim3 grid, hipStream_t s, float* P, float* M, float* V, const void* G, void* Pout,
-                 int64_t n, const AdamCoef& c, const double* d_sq, const int32_t* d_ovf) {
+                 int64_t n, const StepCoef& c, const double* d_sq, const int32_t* d_ovf) {
     hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kEwThreads), kAdamLdsReserve, s, P, M, V, G,
                        static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
 }
 
 template <int GDT>
 void launch_adam_p(dim3 grid, hipStream_t s, bool wp, int pdt, float* P, float* M, float* V, const void* G,
-                   void* Pout, int64_t n, const AdamCoef& c, const double* d_sq, const int32_t* d_ovf) {
+                   void* Pout, int64_t n, const StepCoef& c, const double* d_sq, const int32_t* d_ovf) {
     if (!wp) launch_adam<GDT, ZERO_F16, false>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
     else if (pdt == ZERO_F16) launch_adam<GDT, ZERO_F16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
     else launch_adam<GDT, ZERO_BF16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
@@ -505,19 +494,10 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
         return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
     if (param_out != nullptr && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "unknown param_dtype %d", param_dtype);
-    const zero_adam_params& h = *hp;
-    if (!(h.lr >= 0.0) || !std::isfinite(h.lr)) return fail(ZERO_EINVAL, "lr must be finite and >= 0");
-    if (!(h.beta1 >= 0.0 && h.beta1 < 1.0) || !(h.beta2 >= 0.0 && h.beta2 < 1.0))
-        return fail(ZERO_EINVAL, "betas must lie in [0, 1)");
-    if (!(h.eps >= 0.0) || !std::isfinite(h.eps)) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
-    if (!(h.weight_decay >= 0.0) || !std::isfinite(h.weight_decay))
-        return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
-    if (h.step < 1) return fail(ZERO_EINVAL, "step (1-based index of the step applied) must be >= 1");
-    if (!(h.inv_loss_scale > 0.0) || !std::isfinite(h.inv_loss_scale))
-        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
-    const bool clip = h.max_grad_norm > 0.0;
-    if (clip && !std::isfinite(h.max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm must be finite");
-    if (clip && d_global_sqnorm == nullptr) return fail(ZERO_EINVAL, "clipping needs d_global_sqnorm");
+    StepCoef c;
+    const int pst = prepare_adam(hp, &c);
+    if (pst != ZERO_OK) return pst;
+    if (c.clip && d_global_sqnorm == nullptr) return fail(ZERO_EINVAL, "clipping needs d_global_sqnorm");
     if (n == 0) return ZERO_OK;
     if (!master || !exp_avg || !exp_avg_sq || !grad) return fail(ZERO_EINVAL, "NULL shard pointer");
     if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
@@ -535,25 +515,6 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
         (param_out && (overlaps(param_out, b16, master, b32) || overlaps(param_out, b16, exp_avg, b32) ||
                        overlaps(param_out, b16, exp_avg_sq, b32))))
         return fail(ZERO_EINVAL, "state buffers overlap");
-
-    // per-step coefficients: derived in double, each rounded once to float
-    AdamCoef c;
-    const double t = (double)h.step;
-    const double bc1 = 1.0 - std::pow(h.beta1, t);
-    const double bc2 = 1.0 - std::pow(h.beta2, t);
-    if (!(bc1 > 0.0) || !(bc2 > 0.0)) return fail(ZERO_ERANGE, "bias correction underflows to 0");
-    c.beta1 = (float)h.beta1;
-    c.omb1 = (float)(1.0 - h.beta1);
-    c.beta2 = (float)h.beta2;
-    c.omb2 = (float)(1.0 - h.beta2);
-    c.step_size = (float)(h.lr / bc1);
-    c.rsqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
-    c.eps = (float)h.eps;
-    c.decay = (float)(1.0 - h.lr * h.weight_decay);
-    c.gscale_fixed = (float)h.inv_loss_scale;
-    c.clip = clip ? 1 : 0;
-    c.inv_scale = h.inv_loss_scale;
-    c.max_norm = clip ? h.max_grad_norm : 0.0;
 
     const dim3 grid = elementwise_grid(n);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
