@@ -110,3 +110,20 @@ def test_cpu_entry_points_reject_bad_arguments():
     with pytest.raises(Z.ZeroShardError):
         Z.zero_cpu_shard_adam_step(a, a.copy(), a.copy(), a.copy(), None, Z.AdamHyper(step=0), 0.0, False)
     assert Z.zero_cpu_shard_unscale_norm_overflow(np.zeros(0, np.float32), 1.0) == (0.0, False)
+
+
+def test_worker_pool_survives_fork():
+    """A forked child (which inherits the pool object but none of its
+    threads) still completes host calls, on its own thread."""
+    import os
+    import signal
+    g = np.ones(1 << 20, np.float32)
+    assert Z.zero_cpu_shard_unscale_norm_overflow(g, 1.0) == (float(1 << 20), False)   # pool started
+    pid = os.fork()
+    if pid == 0:
+        signal.alarm(60)
+        ok = Z.zero_cpu_shard_unscale_norm_overflow(g, 1.0) == (float(1 << 20), False)
+        os._exit(0 if ok else 1)
+    _, status = os.waitpid(pid, 0)
+    assert os.WIFEXITED(status) and os.WEXITSTATUS(status) == 0
+    assert Z.zero_cpu_shard_unscale_norm_overflow(g, 2.0) == (4.0 * (1 << 20), False)

@@ -6,18 +6,24 @@
 // norm; clip; bias-corrected AdamW; 16-bit writeback), with the per-step
 // coefficients from the same host routine, on host cores over host memory.
 //
-// Work is cut into fixed chunks of kChunk elements handed to a pool of
-// threads.  The squared norm is summed in float64 per chunk in a fixed order
+// Work is cut into fixed chunks of kChunk elements handed to a persistent
+// pool of threads.  The squared norm is summed in float64 per chunk in a fixed order
 // and the chunk sums are combined in chunk order, so the result does not
 // depend on the number of threads.  The inner loops are written so the
 // compiler vectorizes them; target_clones builds AVX-512, AVX2 and generic
 // versions and picks one at load time.  Floating-point contraction is off, so
 // every version rounds identically.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstring>
+#include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
+
+#include <unistd.h>
 
 #include "common.h"
 #include "zero_shard.h"
@@ -157,22 +163,97 @@ int resolve_threads(int32_t nthreads, int64_t nchunks) {
     return t;
 }
 
+// A persistent pool of worker threads, started on first use and kept for
+// the life of the process, so a call costs a wake-up rather than thread
+// creation.  One job runs at a time (calls from several host threads queue on
+// job_mutex).  A job hands out chunk indices from an atomic counter to the
+// calling thread plus up to threads - 1 workers.
+class Pool {
+  public:
+    static Pool& get() {
+        static Pool pool;
+        return pool;
+    }
+
+    int size() const { return (int)workers_.size() + 1; }
+
+    template <typename F>
+    void run(int64_t nchunks, int threads, F& fn) {
+        std::lock_guard<std::mutex> job(job_mutex_);
+        next_.store(0);
+        auto body = [&]() {
+            for (int64_t c; (c = next_.fetch_add(1)) < nchunks;) fn(c);
+        };
+        // a forked child inherits the pool object but not its threads
+        const int helpers = getpid() == owner_ ? std::min(threads - 1, (int)workers_.size()) : 0;
+        if (helpers <= 0) {
+            body();
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            task_ = [&body]() { body(); };
+            wanted_ = helpers;
+            done_ = 0;
+            ++generation_;
+        }
+        cv_.notify_all();
+        body();
+        std::unique_lock<std::mutex> lk(m_);
+        done_cv_.wait(lk, [&] { return done_ == helpers; });
+        task_ = nullptr;
+    }
+
+  private:
+    Pool() : owner_(getpid()) {
+        const int hw = (int)std::thread::hardware_concurrency();
+        for (int i = 0; i + 1 < (hw > 1 ? hw : 1); ++i) workers_.emplace_back([this, i] { loop(i); });
+    }
+    ~Pool() {
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& t : workers_) t.join();
+    }
+
+    void loop(int index) {
+        uint64_t seen = 0;
+        for (;;) {
+            std::function<void()> task;
+            {
+                std::unique_lock<std::mutex> lk(m_);
+                cv_.wait(lk, [&] { return stop_ || generation_ != seen; });
+                if (stop_) return;
+                seen = generation_;
+                if (index >= wanted_) continue;      // not needed for this job
+                task = task_;
+            }
+            task();
+            {
+                std::lock_guard<std::mutex> lk(m_);
+                ++done_;
+            }
+            done_cv_.notify_one();
+        }
+    }
+
+    const pid_t owner_;
+    std::vector<std::thread> workers_;
+    std::mutex job_mutex_, m_;
+    std::condition_variable cv_, done_cv_;
+    std::function<void()> task_;
+    std::atomic<int64_t> next_{0};
+    uint64_t generation_ = 0;
+    int wanted_ = 0, done_ = 0;
+    bool stop_ = false;
+};
+
 // runs fn(chunk index) for every chunk on `threads` threads (dynamic assignment)
 template <typename F>
 void for_chunks(int64_t nchunks, int threads, F fn) {
-    std::atomic<int64_t> next(0);
-    auto worker = [&]() {
-        for (int64_t c; (c = next.fetch_add(1)) < nchunks;) fn(c);
-    };
-    if (threads <= 1) {
-        worker();
-        return;
-    }
-    std::vector<std::thread> pool;
-    pool.reserve(threads - 1);
-    for (int i = 0; i < threads - 1; ++i) pool.emplace_back(worker);
-    worker();
-    for (auto& t : pool) t.join();
+    Pool::get().run(nchunks, threads, fn);
 }
 
 // decodes gradient elements [e, e + cnt) (cnt <= kTile) to float
