@@ -181,8 +181,15 @@ def main():
                          "gradient directly)")
     ap.add_argument("--offload", action="store_true",
                     help="keep the fp32 state in pinned host memory and step on host cores (CPU offload)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one recorded step graph per step (norm pass, fused update and flag read as a "
+                         "single launch; pays off on small shards where launches dominate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.graph and (args.accum or args.offload):
+        print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum or "
+              "--offload", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on ONE GPU; --gpus {args.gpus} is not supported "
               "(the data-parallel collectives around the step are not part of this build).", file=sys.stderr)
@@ -215,12 +222,14 @@ def main():
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
-                      applied_steps=w.step - 1)
+                      applied_steps=w.step - 1, graph=args.graph)
     K = args.accum
     A = torch.empty(S, dtype=torch.float32, device="cuda") if K else None
     torch.cuda.synchronize()
 
     def step(ev=None):
+        if args.graph and ev is None:
+            return opt.step(G, par)
         if K:
             for k in range(K):
                 if ev is not None and k == K - 1:
@@ -247,10 +256,17 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        skipped += step(evs[k])
+        skipped += step(None if args.graph else evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
+    if args.graph:
+        # a replayed graph has no events between its kernels: the per-kernel
+        # times come from the same kernels launched one by one, after the
+        # timed region
+        for k in range(args.steps):
+            step(evs[k])
+        torch.cuda.synchronize()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
@@ -264,7 +280,7 @@ def main():
     adam_avg = mean(adam_ms)
     adam_gbps = adam_bpp * S / (adam_avg * 1e-3) / 1e9
     step_gbps = step_bpp * S / (ms_step * 1e-3) / 1e9
-    run_key = w.name + (f"+accum{K}" if K else "")
+    run_key = w.name + (f"+accum{K}" if K else "") + ("+graph" if args.graph else "")
     traffic = measured_traffic(run_key)
     accum_stats = None
     if K:
@@ -307,14 +323,16 @@ def main():
                    "flat_offset": begin, "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
                    "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
                    "weight_decay": w.weight_decay, "param_layout": w.param_layout,
-                   "path": f"fp32 gradient accumulation, {K} micro-batches" if K else "16-bit gradient",
+                   "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else "16-bit gradient")
+                   + (", recorded step graph" if args.graph else ""),
                    "algorithmic_bytes_per_param": step_bpp},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "kernel": "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": adam_bpp * S, "avg_ms": adam_avg,
-                     "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9)},
+                     "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9),
+                     "timed_on": "eager launches after the timed region" if args.graph else "the timed steps"},
         "norm_pass": {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9},
         "accumulate": accum_stats,
         "torch_copy_gbps": copy_gbps,

@@ -27,7 +27,8 @@
  *    enqueued: on error no device work has been queued.
  *  - Device functions only enqueue work on `hip_stream` (a hipStream_t; NULL
  *    is the default stream) and return; results are valid once the stream
- *    has reached that point.  They never synchronize and never allocate.
+ *    has reached that point.  They never synchronize and never allocate,
+ *    except the step-graph calls, which say where they do.
  *  - The caller owns every host array and device buffer.  Device pointers
  *    must point to device memory of the current HIP device and be 16-byte
  *    aligned (ZERO_EALIGN otherwise).  The library keeps no state apart from
@@ -180,6 +181,53 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
                          int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
                          const zero_adam_params* hp, const double* d_global_sqnorm,
                          const int32_t* d_global_overflow, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Coefficients in device memory, and recorded step graphs.
+ *
+ * zero_adam_prepare writes the per-step coefficient block that
+ * zero_shard_adam_step derives from hp (zero_adam_coef_bytes() bytes of
+ * plain data; the same validation and errors) into host memory at coef_out.
+ * zero_shard_adam_step_coef is zero_shard_adam_step with that block read
+ * from device memory d_coef (8-byte aligned) when the kernel runs, so a
+ * recorded launch can be replayed with new coefficients; d_global_sqnorm is
+ * required.
+ *
+ * A step graph records, once, on its own stream: the copy of the coefficient
+ * block from pinned host memory, the norm pass (as
+ * zero_shard_unscale_norm_overflow with the given inv_loss_scale, outputs
+ * d_sqnorm / d_overflow, workspace d_workspace), the fused update (as
+ * zero_shard_adam_step_coef, skip and clip from d_overflow / d_sqnorm) and
+ * the copy of the overflow flag back to pinned host memory.  Launching
+ * replays it on hip_stream: one graph launch and one event record per step
+ * instead of four separate calls.  Meant for small shards, where launch
+ * overhead dominates.  The step computed is the one defined above for
+ * zero_shard_unscale_norm_overflow and zero_shard_adam_step (same passages).
+ *  create   records the graph for these buffers and this loss scale.  It
+ *           ALLOCATES (pinned host blocks, a device coefficient block, an
+ *           event, the graph); destroy frees them.  Buffers must outlive it.
+ *  launch   waits for the previous replay, writes hp's coefficients into the
+ *           pinned block, replays.  hp->inv_loss_scale must equal the
+ *           recorded one (ZERO_EINVAL otherwise: record a new graph when the
+ *           loss scale changes).
+ *  overflow waits for the last replay and returns its overflow flag.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOSPC, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+size_t zero_adam_coef_bytes(void);
+int zero_adam_prepare(const zero_adam_params* hp, void* coef_out);
+int zero_shard_adam_step_coef(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                              int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                              const void* d_coef, const double* d_global_sqnorm,
+                              const int32_t* d_global_overflow, void* hip_stream);
+
+typedef struct zero_step_graph zero_step_graph;
+int zero_step_graph_create(zero_step_graph** out, float* master, float* exp_avg, float* exp_avg_sq,
+                           const void* grad, int32_t grad_dtype, void* param_out, int32_t param_dtype,
+                           int64_t n, double inv_loss_scale, double* d_sqnorm, int32_t* d_overflow,
+                           void* d_workspace, size_t workspace_bytes);
+int zero_step_graph_launch(zero_step_graph* g, const zero_adam_params* hp, void* hip_stream);
+int zero_step_graph_overflow(zero_step_graph* g, int32_t* overflow);
+int zero_step_graph_destroy(zero_step_graph* g);
 
 /* ---------------------------------------------------------------------------
  * Gradient accumulation into an fp32 copy (explainer, Ch.02 "The Three

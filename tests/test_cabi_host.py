@@ -172,3 +172,52 @@ def test_workspace_size():
     assert Z.zero_norm_workspace_bytes(-1) == 0
     assert Z.zero_norm_workspace_bytes(1 << 40) <= 2048 * 12 + 256
     assert Z.zero_norm_workspace_bytes(10**6) % 256 == 0
+
+
+def test_coefficient_block_is_the_fp64_formulas_rounded_once():
+    """zero_adam_prepare: each per-step coefficient is its float64 formula
+    rounded once to float32 (lr/(1-b1^t), 1/sqrt(1-b2^t), 1-b, 1-lr*wd)."""
+    import struct
+
+    import numpy as np
+    assert Z.zero_adam_coef_bytes() == struct.calcsize("<9fi2d")
+    for (lr, b1, b2, eps, wd, t, inv, mx) in [(1e-3, 0.9, 0.999, 1e-8, 0.1, 1, 2.0**-16, 1.0),
+                                             (3e-4, 0.95, 0.98, 1e-6, 0.0, 10000, 1.0, 0.0),
+                                             (1e-2, 0.0, 0.0, 0.0, 0.5, 7, 0.25, 2.5)]:
+        buf = np.zeros(Z.zero_adam_coef_bytes(), np.uint8)
+        Z.zero_adam_prepare(Z.AdamHyper(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, step=t,
+                                        inv_loss_scale=inv, max_grad_norm=mx), buf)
+        got = struct.unpack("<9fi2d", buf.tobytes())
+        f32 = lambda x: float(np.float32(x))  # noqa: E731
+        want = (f32(b1), f32(1 - b1), f32(b2), f32(1 - b2), f32(lr / (1 - b1 ** t)), f32(1 / (1 - b2 ** t) ** 0.5),
+                f32(eps), f32(1 - lr * wd), f32(inv), int(mx > 0), inv, mx if mx > 0 else 0.0)
+        assert got == want
+
+
+def test_graph_and_coef_entry_points_reject_bad_arguments_on_host():
+    """Rejected before anything is allocated, recorded or launched."""
+    lib = L.lib()
+    bad = L.zero_adam_params(1e-3, 1.5, 0.999, 1e-8, 0.0, 1, 1.0, 0.0)
+    good = L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 0.0)
+    out = ctypes.create_string_buffer(64)
+    assert lib.zero_adam_prepare(ctypes.byref(bad), out) == L.ZERO_EINVAL
+    assert lib.zero_adam_prepare(ctypes.byref(good), None) == L.ZERO_EINVAL
+    buf = ctypes.create_string_buffer(256)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    step_coef = lib.zero_shard_adam_step_coef
+    assert step_coef(al, al + 16, al + 32, al + 48, 1, None, 0, 4, None, al + 64, None, None) == L.ZERO_EINVAL
+    assert step_coef(al, al + 16, al + 32, al + 48, 1, None, 0, 4, al + 96, None, None, None) == L.ZERO_EINVAL
+    assert step_coef(al, al + 16, al + 32, al + 48, 7, None, 0, 4, al + 96, al + 64, None, None) == L.ZERO_EINVAL
+    h = ctypes.c_void_p()
+    create = lib.zero_step_graph_create
+    assert create(None, al, al + 16, al + 32, al + 48, 1, None, 0, 4, 1.0, al + 64, al + 72, al + 128, 1024) == L.ZERO_EINVAL
+    assert create(ctypes.byref(h), al, al + 16, al + 32, al + 48, 1, None, 0, 4, 0.0, al + 64, al + 72, al + 128,
+                  1024) == L.ZERO_EINVAL
+    assert create(ctypes.byref(h), al, al + 16, al + 32, al + 48, 1, None, 0, 4, 1.0, al + 64, al + 72, al + 128,
+                  0) == L.ZERO_ENOSPC
+    assert create(ctypes.byref(h), al, al, al + 32, al + 48, 1, None, 0, 4, 1.0, al + 64, al + 72, al + 128,
+                  1024) == L.ZERO_EINVAL                                   # master aliases exp_avg
+    assert h.value is None
+    assert lib.zero_step_graph_launch(None, ctypes.byref(good), None) == L.ZERO_EINVAL
+    assert lib.zero_step_graph_overflow(None, None) == L.ZERO_EINVAL
+    assert lib.zero_step_graph_destroy(None) == L.ZERO_OK

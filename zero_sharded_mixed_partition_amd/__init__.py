@@ -29,7 +29,8 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "zero_cpu_shard_unscale_norm_overflow", "zero_cpu_shard_adam_step",
            "zero_loss_scaler_update", "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZERO_F32",
            "ZeroShardError", "AdamHyper",
-           "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam"]
+           "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam", "StepGraph", "zero_adam_coef_bytes",
+           "zero_adam_prepare", "zero_shard_adam_step_coef"]
 
 
 def zero_abi_version() -> int:
@@ -223,6 +224,74 @@ def zero_cpu_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: A
                                                _host_ptr(grad), gd, _host_ptr(param_out), pd, n, ctypes.byref(params),
                                                float(global_sqnorm), 1 if global_overflow else 0, int(nthreads)),
              "zero_cpu_shard_adam_step")
+
+
+def zero_adam_coef_bytes() -> int:
+    return int(_L.lib().zero_adam_coef_bytes())
+
+
+def zero_adam_prepare(hp: AdamHyper, coef_out) -> None:
+    """Per-step coefficient block of hp into host memory coef_out (a CPU uint8
+    tensor or numpy array of zero_adam_coef_bytes() bytes, or an address)."""
+    params = hp.c()
+    addr = coef_out if isinstance(coef_out, int) else _host_ptr(coef_out)
+    _L.check(_L.lib().zero_adam_prepare(ctypes.byref(params), addr), "zero_adam_prepare")
+
+
+def zero_shard_adam_step_coef(master, exp_avg, exp_avg_sq, grad, param_out, d_coef, global_sqnorm,
+                              global_overflow=None, grad_dtype: Optional[int] = None,
+                              param_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """zero_shard_adam_step with the coefficient block read from device memory d_coef."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
+    n = master.numel() if n is None else n
+    _L.check(_L.lib().zero_shard_adam_step_coef(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
+                                                _ptr(param_out), pd, n, _ptr(d_coef), _ptr(global_sqnorm),
+                                                _ptr(global_overflow), _stream(stream)),
+             "zero_shard_adam_step_coef")
+
+
+class StepGraph:
+    """A recorded step (coefficients in, norm pass, fused update, flag out)
+    over fixed buffers and a fixed loss scale; see zero_step_graph_* in the
+    header.  The library allocates its pinned and device blocks; close()
+    (or garbage collection) frees them."""
+
+    def __init__(self, master, exp_avg, exp_avg_sq, grad, param_out, inv_loss_scale: float, sqnorm, overflow,
+                 workspace, grad_dtype: Optional[int] = None, param_dtype: Optional[int] = None):
+        gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+        pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
+        handle = ctypes.c_void_p()
+        wbytes = workspace.numel() * workspace.element_size()
+        _L.check(_L.lib().zero_step_graph_create(ctypes.byref(handle), _ptr(master), _ptr(exp_avg),
+                                                 _ptr(exp_avg_sq), _ptr(grad), gd, _ptr(param_out), pd,
+                                                 master.numel(), float(inv_loss_scale), _ptr(sqnorm),
+                                                 _ptr(overflow), _ptr(workspace), wbytes),
+                 "zero_step_graph_create")
+        self._h = handle.value
+        self.inv_loss_scale = float(inv_loss_scale)
+        self._keep = (master, exp_avg, exp_avg_sq, grad, param_out, sqnorm, overflow, workspace)
+
+    def launch(self, hp: AdamHyper, stream=None) -> None:
+        params = hp.c()
+        _L.check(_L.lib().zero_step_graph_launch(self._h, ctypes.byref(params), _stream(stream)),
+                 "zero_step_graph_launch")
+
+    def overflow(self) -> bool:
+        flag = ctypes.c_int32()
+        _L.check(_L.lib().zero_step_graph_overflow(self._h, ctypes.byref(flag)), "zero_step_graph_overflow")
+        return bool(flag.value)
+
+    def close(self) -> None:
+        if self._h:
+            _L.lib().zero_step_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class LossScaler:

@@ -35,6 +35,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "common.h"
 #include "zero_shard.h"
@@ -283,14 +284,10 @@ __device__ __forceinline__ void adam_elem(const StepCoef& c, float gscale, float
 }
 
 template <int GDT, int PDT, bool WRITE_P>
-__global__ __launch_bounds__(kEwThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
-                                                          float* __restrict__ V, const void* __restrict__ G,
-                                                          uint16_t* __restrict__ Pout, int64_t n, StepCoef c,
-                                                          const double* __restrict__ d_sq,
-                                                          const int32_t* __restrict__ d_ovf) {
-    // Dynamic LDS reserved by the launcher only to cap how many of these
-    // workgroups (one wave each) are resident per CU; it is never read.
-    extern __shared__ float occupancy_pad[];
+__device__ __forceinline__ void adam_body(float* __restrict__ P, float* __restrict__ M, float* __restrict__ V,
+                                          const void* __restrict__ G, uint16_t* __restrict__ Pout, int64_t n,
+                                          const StepCoef& c, const double* __restrict__ d_sq,
+                                          const int32_t* __restrict__ d_ovf, float* occupancy_pad) {
     // skipped step: the whole grid sees the same flag and writes nothing
     if (d_ovf != nullptr && *d_ovf != 0) return;
     float gscale = c.gscale_fixed;
@@ -344,6 +341,33 @@ __global__ __launch_bounds__(kEwThreads) void adam_update(float* __restrict__ P,
         }
     }
     if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
+}
+
+// Coefficients by value (one launch per step).
+template <int GDT, int PDT, bool WRITE_P>
+__global__ __launch_bounds__(kEwThreads) void adam_update(float* __restrict__ P, float* __restrict__ M,
+                                                          float* __restrict__ V, const void* __restrict__ G,
+                                                          uint16_t* __restrict__ Pout, int64_t n, StepCoef c,
+                                                          const double* __restrict__ d_sq,
+                                                          const int32_t* __restrict__ d_ovf) {
+    // Dynamic LDS reserved by the launcher only to cap how many of these
+    // workgroups (one wave each) are resident per CU; it is never read.
+    extern __shared__ float occupancy_pad[];
+    adam_body<GDT, PDT, WRITE_P>(P, M, V, G, Pout, n, c, d_sq, d_ovf, occupancy_pad);
+}
+
+// Coefficients read from device memory at run time, so a captured graph can
+// be replayed with the coefficients of each new step.
+template <int GDT, int PDT, bool WRITE_P>
+__global__ __launch_bounds__(kEwThreads) void adam_update_devcoef(float* __restrict__ P, float* __restrict__ M,
+                                                                  float* __restrict__ V, const void* __restrict__ G,
+                                                                  uint16_t* __restrict__ Pout, int64_t n,
+                                                                  const StepCoef* __restrict__ pc,
+                                                                  const double* __restrict__ d_sq,
+                                                                  const int32_t* __restrict__ d_ovf) {
+    extern __shared__ float occupancy_pad[];
+    const StepCoef c = *pc;
+    adam_body<GDT, PDT, WRITE_P>(P, M, V, G, Pout, n, c, d_sq, d_ovf, occupancy_pad);
 }
 
 // ---------------------------------------------------------------- gradient accumulation
@@ -420,19 +444,61 @@ void launch_norm(int nb, hipStream_t s, const void* grad, int64_t n, double* par
                        tail, tail_n, part_sq, part_bad);
 }
 
+// d_coef == nullptr: coefficients c by value; otherwise read from d_coef on the device
 template <int GDT, int PDT, bool WRITE_P>
 void launch_adam(dim3 grid, hipStream_t s, float* P, float* M, float* V, const void* G, void* Pout,
-                 int64_t n, const StepCoef& c, const double* d_sq, const int32_t* d_ovf) {
-    hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kEwThreads), kAdamLdsReserve, s, P, M, V, G,
-                       static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
+                 int64_t n, const StepCoef& c, const StepCoef* d_coef, const double* d_sq, const int32_t* d_ovf) {
+    if (d_coef == nullptr)
+        hipLaunchKernelGGL((adam_update<GDT, PDT, WRITE_P>), grid, dim3(kEwThreads), kAdamLdsReserve, s, P, M, V,
+                           G, static_cast<uint16_t*>(Pout), n, c, d_sq, d_ovf);
+    else
+        hipLaunchKernelGGL((adam_update_devcoef<GDT, PDT, WRITE_P>), grid, dim3(kEwThreads), kAdamLdsReserve, s,
+                           P, M, V, G, static_cast<uint16_t*>(Pout), n, d_coef, d_sq, d_ovf);
 }
 
 template <int GDT>
 void launch_adam_p(dim3 grid, hipStream_t s, bool wp, int pdt, float* P, float* M, float* V, const void* G,
-                   void* Pout, int64_t n, const StepCoef& c, const double* d_sq, const int32_t* d_ovf) {
-    if (!wp) launch_adam<GDT, ZERO_F16, false>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
-    else if (pdt == ZERO_F16) launch_adam<GDT, ZERO_F16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
-    else launch_adam<GDT, ZERO_BF16, true>(grid, s, P, M, V, G, Pout, n, c, d_sq, d_ovf);
+                   void* Pout, int64_t n, const StepCoef& c, const StepCoef* d_coef, const double* d_sq,
+                   const int32_t* d_ovf) {
+    if (!wp) launch_adam<GDT, ZERO_F16, false>(grid, s, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+    else if (pdt == ZERO_F16) launch_adam<GDT, ZERO_F16, true>(grid, s, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+    else launch_adam<GDT, ZERO_BF16, true>(grid, s, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+}
+
+void launch_adam_any(int32_t gdt, dim3 grid, hipStream_t s, bool wp, int pdt, float* P, float* M, float* V,
+                     const void* G, void* Pout, int64_t n, const StepCoef& c, const StepCoef* d_coef,
+                     const double* d_sq, const int32_t* d_ovf) {
+    if (gdt == ZERO_F16) launch_adam_p<ZERO_F16>(grid, s, wp, pdt, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+    else if (gdt == ZERO_BF16) launch_adam_p<ZERO_BF16>(grid, s, wp, pdt, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+    else launch_adam_p<ZERO_F32>(grid, s, wp, pdt, P, M, V, G, Pout, n, c, d_coef, d_sq, d_ovf);
+}
+
+// argument checks shared by the AdamW entry points (coefficients aside)
+int check_step_args(float* master, float* exp_avg, float* exp_avg_sq, const void* grad, int32_t grad_dtype,
+                    void* param_out, int32_t param_dtype, int64_t n, const double* d_sq, const int32_t* d_ovf) {
+    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
+        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
+    if (param_out != nullptr && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "unknown param_dtype %d", param_dtype);
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !grad) return fail(ZERO_EINVAL, "NULL shard pointer");
+    if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
+        (param_out && !aligned16(param_out)))
+        return fail(ZERO_EALIGN, "shard pointers must be 16-byte aligned");
+    if (d_sq && ((uintptr_t)d_sq & 7u)) return fail(ZERO_EALIGN, "d_global_sqnorm misaligned");
+    if (d_ovf && ((uintptr_t)d_ovf & 3u)) return fail(ZERO_EALIGN, "d_global_overflow misaligned");
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    const int64_t b32 = n * 4, b16 = n * 2, bg = n * grad_bytes(grad_dtype);
+    if (overlaps(grad, bg, master, b32) || overlaps(grad, bg, exp_avg, b32) || overlaps(grad, bg, exp_avg_sq, b32) ||
+        (param_out && overlaps(grad, bg, param_out, b16)))
+        return fail(ZERO_EINVAL, "grad aliases an output");
+    if (overlaps(master, b32, exp_avg, b32) || overlaps(master, b32, exp_avg_sq, b32) ||
+        overlaps(exp_avg, b32, exp_avg_sq, b32) ||
+        (param_out && (overlaps(param_out, b16, master, b32) || overlaps(param_out, b16, exp_avg, b32) ||
+                       overlaps(param_out, b16, exp_avg_sq, b32))))
+        return fail(ZERO_EINVAL, "state buffers overlap");
+    return ZERO_OK;
 }
 
 }  // namespace
@@ -488,47 +554,46 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
                          void* param_out, int32_t param_dtype, int64_t n, const zero_adam_params* hp,
                          const double* d_global_sqnorm, const int32_t* d_global_overflow, void* hip_stream) {
     clear_error();
-    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
-    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
-    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
-        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
-    if (param_out != nullptr && param_dtype != ZERO_F16 && param_dtype != ZERO_BF16)
-        return fail(ZERO_EINVAL, "unknown param_dtype %d", param_dtype);
     StepCoef c;
     const int pst = prepare_adam(hp, &c);
     if (pst != ZERO_OK) return pst;
     if (c.clip && d_global_sqnorm == nullptr) return fail(ZERO_EINVAL, "clipping needs d_global_sqnorm");
-    if (n == 0) return ZERO_OK;
-    if (!master || !exp_avg || !exp_avg_sq || !grad) return fail(ZERO_EINVAL, "NULL shard pointer");
-    if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq) || !aligned16(grad) ||
-        (param_out && !aligned16(param_out)))
-        return fail(ZERO_EALIGN, "shard pointers must be 16-byte aligned");
-    if (d_global_sqnorm && ((uintptr_t)d_global_sqnorm & 7u)) return fail(ZERO_EALIGN, "d_global_sqnorm misaligned");
-    if (d_global_overflow && ((uintptr_t)d_global_overflow & 3u)) return fail(ZERO_EALIGN, "d_global_overflow misaligned");
-    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
-    const int64_t b32 = n * 4, b16 = n * 2, bg = n * grad_bytes(grad_dtype);
-    if (overlaps(grad, bg, master, b32) || overlaps(grad, bg, exp_avg, b32) || overlaps(grad, bg, exp_avg_sq, b32) ||
-        (param_out && overlaps(grad, bg, param_out, b16)))
-        return fail(ZERO_EINVAL, "grad aliases an output");
-    if (overlaps(master, b32, exp_avg, b32) || overlaps(master, b32, exp_avg_sq, b32) ||
-        overlaps(exp_avg, b32, exp_avg_sq, b32) ||
-        (param_out && (overlaps(param_out, b16, master, b32) || overlaps(param_out, b16, exp_avg, b32) ||
-                       overlaps(param_out, b16, exp_avg_sq, b32))))
-        return fail(ZERO_EINVAL, "state buffers overlap");
-
-    const dim3 grid = elementwise_grid(n);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const bool wp = param_out != nullptr;
-    if (grad_dtype == ZERO_F16)
-        launch_adam_p<ZERO_F16>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
-                                d_global_sqnorm, d_global_overflow);
-    else if (grad_dtype == ZERO_BF16)
-        launch_adam_p<ZERO_BF16>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
-                                 d_global_sqnorm, d_global_overflow);
-    else
-        launch_adam_p<ZERO_F32>(grid, s, wp, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c,
-                                d_global_sqnorm, d_global_overflow);
+    const int st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n,
+                                   d_global_sqnorm, d_global_overflow);
+    if (st != ZERO_OK || n == 0) return st;
+    launch_adam_any(grad_dtype, elementwise_grid(n), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
+                    param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c, nullptr, d_global_sqnorm,
+                    d_global_overflow);
     return launch_status("adam_update");
+}
+
+size_t zero_adam_coef_bytes(void) { return sizeof(StepCoef); }
+
+int zero_adam_prepare(const zero_adam_params* hp, void* coef_out) {
+    clear_error();
+    if (coef_out == nullptr) return fail(ZERO_EINVAL, "coef_out is NULL");
+    StepCoef c;
+    const int pst = prepare_adam(hp, &c);
+    if (pst != ZERO_OK) return pst;
+    std::memcpy(coef_out, &c, sizeof(c));
+    return ZERO_OK;
+}
+
+int zero_shard_adam_step_coef(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                              int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                              const void* d_coef, const double* d_global_sqnorm,
+                              const int32_t* d_global_overflow, void* hip_stream) {
+    clear_error();
+    if (d_coef == nullptr || ((uintptr_t)d_coef & 7u)) return fail(ZERO_EINVAL, "d_coef NULL or not 8-byte aligned");
+    if (d_global_sqnorm == nullptr) return fail(ZERO_EINVAL, "d_global_sqnorm is required");
+    const int st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n,
+                                   d_global_sqnorm, d_global_overflow);
+    if (st != ZERO_OK || n == 0) return st;
+    const StepCoef unused{};
+    launch_adam_any(grad_dtype, elementwise_grid(n), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
+                    param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, unused,
+                    static_cast<const StepCoef*>(d_coef), d_global_sqnorm, d_global_overflow);
+    return launch_status("adam_update_devcoef");
 }
 
 int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
@@ -559,6 +624,127 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
     }
 #undef ZS_ACC
     return launch_status("grad_accumulate");
+}
+
+// ---------------------------------------------------------------- step graphs
+
+struct zero_step_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;       // recorded after every launch
+    StepCoef* h_coef = nullptr;      // pinned host: the next step's coefficients
+    int32_t* h_flag = nullptr;       // pinned host: the last step's overflow flag
+    StepCoef* d_coef = nullptr;      // device copy read by the update kernel
+    double inv_loss_scale = 1.0;
+    bool launched = false;
+};
+
+static void release_graph(zero_step_graph* g) {
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    if (g->done) (void)hipEventDestroy(g->done);
+    if (g->h_coef) (void)hipHostFree(g->h_coef);
+    if (g->h_flag) (void)hipHostFree(g->h_flag);
+    if (g->d_coef) (void)hipFree(g->d_coef);
+    delete g;
+}
+
+int zero_step_graph_create(zero_step_graph** out, float* master, float* exp_avg, float* exp_avg_sq,
+                           const void* grad, int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                           double inv_loss_scale, double* d_sqnorm, int32_t* d_overflow, void* d_workspace,
+                           size_t workspace_bytes) {
+    clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    if (d_sqnorm == nullptr || d_overflow == nullptr || d_workspace == nullptr)
+        return fail(ZERO_EINVAL, "NULL norm output or workspace");
+    if (((uintptr_t)d_sqnorm & 7u) || ((uintptr_t)d_overflow & 3u) || !aligned16(d_workspace))
+        return fail(ZERO_EALIGN, "norm outputs or workspace misaligned");
+    if (workspace_bytes < zero_norm_workspace_bytes(n)) return fail(ZERO_ENOSPC, "workspace too small");
+    int st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n, d_sqnorm,
+                             d_overflow);
+    if (st != ZERO_OK) return st;
+    zero_step_graph* g = new zero_step_graph();
+    g->inv_loss_scale = inv_loss_scale;
+    hipStream_t cs = nullptr;
+    hipError_t e = hipHostMalloc((void**)&g->h_coef, sizeof(StepCoef), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&g->h_flag, sizeof(int32_t), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipMalloc((void**)&g->d_coef, sizeof(StepCoef));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&g->done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreate(&cs);
+    if (e != hipSuccess) {
+        if (cs) (void)hipStreamDestroy(cs);
+        release_graph(g);
+        return fail(ZERO_EHIP, "step graph resources: %s", hipGetErrorString(e));
+    }
+    std::memset(g->h_coef, 0, sizeof(StepCoef));
+    *g->h_flag = 0;
+    // record: coefficients in, norm pass, fused update, flag out
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        e = hipMemcpyAsync(g->d_coef, g->h_coef, sizeof(StepCoef), hipMemcpyHostToDevice, cs);
+        if (e == hipSuccess)
+            st = zero_shard_unscale_norm_overflow(grad, grad_dtype, n, inv_loss_scale, d_sqnorm, d_overflow,
+                                                  d_workspace, workspace_bytes, cs);
+        if (e == hipSuccess && st == ZERO_OK)
+            st = zero_shard_adam_step_coef(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n,
+                                           g->d_coef, d_sqnorm, d_overflow, cs);
+        if (e == hipSuccess && st == ZERO_OK)
+            e = hipMemcpyAsync(g->h_flag, d_overflow, sizeof(int32_t), hipMemcpyDeviceToHost, cs);
+        const hipError_t e2 = hipStreamEndCapture(cs, &g->graph);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e == hipSuccess && st == ZERO_OK) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cs);
+    if (e != hipSuccess || st != ZERO_OK) {
+        release_graph(g);
+        if (st != ZERO_OK) return st;
+        return fail(ZERO_EHIP, "step graph capture: %s", hipGetErrorString(e));
+    }
+    *out = g;
+    return ZERO_OK;
+}
+
+int zero_step_graph_launch(zero_step_graph* g, const zero_adam_params* hp, void* hip_stream) {
+    clear_error();
+    if (g == nullptr) return fail(ZERO_EINVAL, "graph is NULL");
+    StepCoef c;
+    const int pst = prepare_adam(hp, &c);
+    if (pst != ZERO_OK) return pst;
+    if (hp->inv_loss_scale != g->inv_loss_scale)
+        return fail(ZERO_EINVAL, "inv_loss_scale differs from the one the graph was recorded with");
+    // the previous replay may still be reading the pinned coefficient block
+    if (g->launched) {
+        const hipError_t e = hipEventSynchronize(g->done);
+        if (e != hipSuccess) return fail(ZERO_EHIP, "waiting for the previous replay: %s", hipGetErrorString(e));
+    }
+    std::memcpy(g->h_coef, &c, sizeof(c));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipGraphLaunch(g->exec, s);
+    if (e == hipSuccess) e = hipEventRecord(g->done, s);
+    if (e != hipSuccess) return fail(ZERO_EHIP, "graph launch: %s", hipGetErrorString(e));
+    g->launched = true;
+    return ZERO_OK;
+}
+
+int zero_step_graph_overflow(zero_step_graph* g, int32_t* overflow) {
+    clear_error();
+    if (g == nullptr || overflow == nullptr) return fail(ZERO_EINVAL, "NULL argument");
+    if (!g->launched) return fail(ZERO_EINVAL, "graph not launched yet");
+    const hipError_t e = hipEventSynchronize(g->done);
+    if (e != hipSuccess) return fail(ZERO_EHIP, "waiting for the replay: %s", hipGetErrorString(e));
+    *overflow = *g->h_flag != 0 ? 1 : 0;
+    return ZERO_OK;
+}
+
+int zero_step_graph_destroy(zero_step_graph* g) {
+    clear_error();
+    if (g == nullptr) return ZERO_OK;
+    if (g->launched) (void)hipEventSynchronize(g->done);
+    release_graph(g);
+    return ZERO_OK;
 }
 
 }  // extern "C"

@@ -13,14 +13,15 @@ from typing import Callable, Optional
 
 import torch
 
-from . import (ZERO_F32, AdamHyper, LossScaler, dtype_code, zero_loss_scaler_update, zero_norm_workspace_bytes,
-               zero_shard_adam_step, zero_shard_grad_accumulate, zero_shard_unscale_norm_overflow)
+from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, dtype_code, zero_loss_scaler_update,
+               zero_norm_workspace_bytes, zero_shard_adam_step, zero_shard_grad_accumulate,
+               zero_shard_unscale_norm_overflow)
 
 
 class ShardAdam:
     def __init__(self, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, *,
                  lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=0.0,
-                 scaler: Optional[LossScaler] = None, applied_steps: int = 0):
+                 scaler: Optional[LossScaler] = None, applied_steps: int = 0, graph: bool = False):
         n = master.numel()
         for t in (master, exp_avg, exp_avg_sq):
             if t.dtype != torch.float32 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
@@ -36,6 +37,11 @@ class ShardAdam:
         self.overflow = torch.empty(1, dtype=torch.int32, device=dev)
         self._flag_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
         self._flag_ready = torch.cuda.Event()
+        # graph mode: one recorded step replayed per step (re-recorded when the
+        # buffers or the loss scale change); used when no all-reduce hook is given
+        self.graph = graph
+        self._graph, self._graph_key = None, None
+        self.recorded_this_step = False
 
     def _inv_scale(self, grad: torch.Tensor) -> float:
         # an fp32 gradient is the accumulation copy, already unscaled
@@ -77,8 +83,27 @@ class ShardAdam:
         this rank's two scalars into the data-parallel sum / OR in place (on
         one GPU the shard's own values are the global ones).  Returns True if
         the step was skipped."""
+        if self.graph and allreduce is None:
+            return self._graph_step(grad, param_out)
         self.unscale_norm(grad)
         if allreduce is not None:
             allreduce(self.sqnorm, self.overflow)
         self.apply(grad, param_out)
         return self.finish()
+
+    def _graph_step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor]) -> bool:
+        inv = self._inv_scale(grad)
+        key = (grad.data_ptr(), grad.dtype, grad.numel(),
+               None if param_out is None else (param_out.data_ptr(), param_out.dtype), inv)
+        self.recorded_this_step = key != self._graph_key
+        if self.recorded_this_step:
+            if self._graph is not None:
+                self._graph.close()
+            self._graph = StepGraph(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out, inv, self.sqnorm,
+                                    self.overflow, self.workspace)
+            self._graph_key = key
+        self._graph.launch(AdamHyper(step=self.t + 1, inv_loss_scale=inv, **self.hyper))
+        skip = zero_loss_scaler_update(self.scaler, self._graph.overflow())
+        if not skip:
+            self.t += 1
+        return skip
