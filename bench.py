@@ -79,37 +79,72 @@ def upload_inputs(w, begin, S, grad_dtype, block_chunks=16):
     return P, M, V, G
 
 
-def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24):
-    """The CPU oracle's full step (exact norm + AdamW; with `accum` > 0, that
-    many micro-batch accumulations into the fp32 copy first) on a bounded
-    sample of the same shard: consecutive blocks of 2^24 parameters from its
-    start, one process, until at least `target_s` seconds of oracle time."""
+def _oracle_block(w, lo, n, accum, threads=0):
+    """Seconds of oracle time for one full step (exact norm + AdamW; with
+    `accum` > 0, that many micro-batch accumulations into the fp32 copy
+    first) on flat parameters [lo, lo+n); input generation excluded."""
     import oracle
     import workloads as W
 
-    inv = 1.0 / w.loss_scale
+    p, m, v, g = W.shard_inputs(w, lo, n, threads=threads)
+    t0 = time.perf_counter()
+    gfmt, ginv = w.grad_dtype, 1.0 / w.loss_scale
+    if accum:
+        acc = None
+        for _ in range(accum):
+            acc, _ovf = oracle.grad_accumulate(acc, g, w.grad_dtype, ginv)
+        g, gfmt, ginv = acc, "f32", 1.0
+    sq, ovf = oracle.shard_sqnorm_overflow(g, gfmt, ginv)
+    oracle.shard_step(p, m, v, g, gfmt, w.param_dtype, global_sq=sq, global_overflow=ovf,
+                      inv_loss_scale=ginv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
+                      beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.step)
+    return time.perf_counter() - t0
+
+
+def _oracle_worker(job):
+    """One process of the all-cores leg: its blocks one after another, one thread."""
+    w, blocks, accum = job
+    if w.grad_dtype == "bf16":          # the bf16 input cast goes through torch's CPU kernels
+        import torch
+        torch.set_num_threads(1)
+    spent = 0.0
+    for lo, n in blocks:
+        spent += _oracle_block(w, lo, n, accum, threads=1)
+    return sum(n for _, n in blocks), spent
+
+
+def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, max_procs=16):
+    """The CPU oracle timed on a bounded sample of the same shard, blocks of
+    consecutive parameters from its start, one step per block:
+      all cores  one process per host core (at most `max_procs`), two blocks
+                 of `par_block` each; rate = sampled params / the busiest
+                 process's oracle time;
+      one core   one process, blocks of `block` until `target_s` seconds of
+                 oracle time.
+    Runs before the GPU is touched (workers are forked)."""
+    import multiprocessing
+
+    cores = max(1, min(max_procs, len(os.sched_getaffinity(0))))
+    nblk = min(2 * cores, -(-S // par_block))
+    blocks = [(begin + k * par_block, min(par_block, S - k * par_block)) for k in range(nblk)]
+    jobs = [(w, blocks[j::cores], accum) for j in range(cores) if blocks[j::cores]]
+    with multiprocessing.get_context("fork").Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    par_done, par_time = sum(r[0] for r in res), max(r[1] for r in res)
+
     done, spent = 0, 0.0
     while spent < target_s and done < S:
         n = min(block, S - done)
-        p, m, v, g = W.shard_inputs(w, begin + done, n)
-        t0 = time.perf_counter()
-        gfmt, ginv = w.grad_dtype, inv
-        if accum:
-            acc = None
-            for _ in range(accum):
-                acc, _ovf = oracle.grad_accumulate(acc, g, w.grad_dtype, inv)
-            g, gfmt, ginv = acc, "f32", 1.0
-        sq, ovf = oracle.shard_sqnorm_overflow(g, gfmt, ginv)
-        oracle.shard_step(p, m, v, g, gfmt, w.param_dtype, global_sq=sq, global_overflow=ovf,
-                          inv_loss_scale=ginv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
-                          beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=w.step)
-        spent += time.perf_counter() - t0
+        spent += _oracle_block(w, begin + done, n, accum)
         done += n
     what = f"{accum} accumulations + " if accum else ""
-    return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of the shard's {S} params in blocks of {block}, one step each "
-                      f"({what}exact norm + AdamW, float64 NumPy, one process); {spent:.1f} s of oracle time, "
-                      f"input generation excluded"}
+    return {"value": par_done / par_time, "unit": "params/s", "cores": len(jobs), "kind": "oracle",
+            "sample": f"first {par_done} of the shard's {S} params in blocks of {par_block}, one step each "
+                      f"({what}exact norm + AdamW, float64 NumPy), {len(jobs)} processes of one thread "
+                      f"each; busiest process {par_time:.1f} s of oracle time, input generation excluded",
+            "one_core": {"value": done / spent, "cores": 1,
+                         "sample": f"first {done} params in blocks of {block}, one process, {spent:.1f} s of "
+                                   f"oracle time"}}
 
 
 def bench_offload(w, args):
@@ -203,11 +238,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        # before the GPU is touched (the oracle is host-only)
-        import zero_sharded_mixed_partition_amd as Z
-        _, S0, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+        # first, before torch or the GPU is touched: the oracle is host-only
+        # and its all-cores leg forks worker processes
+        import oracle
+        _, S0, _ = oracle.partition_plan(w.shapes, w.n_d, w.align)
         cpu = cpu_baseline(w, w.rank * S0, S0, accum=args.accum)
-        print(f"# cpu baseline {cpu['value']:.4g} params/s", file=sys.stderr, flush=True)
+        print(f"# cpu baseline {cpu['value']:.4g} params/s on {cpu['cores']} cores, "
+              f"{cpu['one_core']['value']:.4g} on one", file=sys.stderr, flush=True)
 
     import torch
 
@@ -253,10 +290,13 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     skipped = 0
+    wall = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        skipped += step(None if args.graph else evs[k])
+        ts = time.perf_counter()
+        skipped += step(None if args.graph else evs[k])      # ends with the flag read: the step is done
+        wall.append(time.perf_counter() - ts)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
@@ -267,6 +307,21 @@ def main():
         for k in range(args.steps):
             step(evs[k])
         torch.cuda.synchronize()
+
+    # skipped steps, timed apart: +inf in one gradient element makes the norm
+    # pass raise the flag and the update exit without touching the state
+    n_skip = min(10, args.steps)
+    keep = G[S // 2].clone()
+    G[S // 2] = float("inf")
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_skip)]
+    torch.cuda.synchronize()
+    skip_wall = []
+    for k in range(n_skip):
+        ts = time.perf_counter()
+        assert step(sev[k]), "a gradient holding +inf must skip the step"
+        skip_wall.append(time.perf_counter() - ts)
+    G[S // 2] = keep
+    torch.cuda.synchronize()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
@@ -290,20 +345,27 @@ def main():
                        "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
                        "traffic": measured_traffic(run_key, "grad_accumulate")}
 
-    # context: torch's device-to-device copy (the runtime's blit kernel) over
-    # the same 14 B/param read + 14 B/param write; also the known-size copy
-    # that scales the HBM byte counters
-    src = torch.empty(S * 14 // 4, dtype=torch.float32, device="cuda")
+    # the achievable rate of one read + one write stream over the same 14 B/param
+    # each way (at most 16 GiB): the library's reference copy kernel, and
+    # torch's device-to-device copy (the runtime's blit kernel, also the
+    # known-size copy that scales the HBM byte counters)
+    cbytes = min(S * 14, 16 << 30) // 16 * 16
+    src = torch.empty(cbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+
+    def time_copy(fn):
+        for _ in range(3):
+            fn()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            fn()
+        c1.record()
+        torch.cuda.synchronize()
+        return 2 * cbytes / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+
+    ref_gbps = time_copy(lambda: Z.zero_copy_reference(dst, src, cbytes))
+    copy_gbps = time_copy(lambda: dst.copy_(src))
     del src, dst
 
     out = {
@@ -333,7 +395,15 @@ def main():
                      "algorithmic_bytes": adam_bpp * S, "avg_ms": adam_avg,
                      "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9),
                      "timed_on": "eager launches after the timed region" if args.graph else "the timed steps"},
+        "step_ms": {"median": pct(sorted(wall), 0.5) * 1e3, "p10": pct(sorted(wall), 0.1) * 1e3,
+                    "p90": pct(sorted(wall), 0.9) * 1e3},
         "norm_pass": {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9},
+        "skipped_step": {"steps": n_skip, "ms_per_step": mean(skip_wall) * 1e3,
+                         "norm_ms": mean([e[0].elapsed_time(e[1]) for e in sev]),
+                         "update_ms": mean([e[1].elapsed_time(e[2]) for e in sev])},
+        "copy_reference": {"kernel": "copy16 (zero_copy_reference)", "bytes_each_way": cbytes, "gbps": ref_gbps,
+                           "frac_of_peak": ref_gbps / PEAK_HBM_GBPS, "adam_update_frac_of_copy": adam_gbps / ref_gbps,
+                           "step_frac_of_copy": step_gbps / ref_gbps},
         "accumulate": accum_stats,
         "torch_copy_gbps": copy_gbps,
         "skipped_steps": skipped,

@@ -296,6 +296,17 @@ typedef struct {
 
 int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not a step of the method): a plain device copy, one
+ * 16-byte vector per lane, in the same streaming style as the step's kernels.
+ * Its rate is the achievable rate of one read plus one write stream, which
+ * the step's kernels are reported against beside the nominal HBM peak.
+ * Async on hip_stream.  dst, src: device, 16-byte aligned, not overlapping;
+ * bytes: a multiple of 16 (0 is a no-op).
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+int zero_copy_reference(void* dst, const void* src, int64_t bytes, void* hip_stream);
+
 /* Static description of a status code, and the thread-local detail of the
  * last failing call (empty string if none). */
 const char* zero_status_string(int status);

@@ -221,3 +221,17 @@ def test_graph_and_coef_entry_points_reject_bad_arguments_on_host():
     assert lib.zero_step_graph_launch(None, ctypes.byref(good), None) == L.ZERO_EINVAL
     assert lib.zero_step_graph_overflow(None, None) == L.ZERO_EINVAL
     assert lib.zero_step_graph_destroy(None) == L.ZERO_OK
+
+
+def test_copy_reference_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(256)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    cp = lib.zero_copy_reference
+    assert cp(al, al + 64, 0, None) == L.ZERO_OK                    # empty: nothing launched
+    assert cp(al, al + 64, 24, None) == L.ZERO_EINVAL               # not a multiple of 16
+    assert cp(al, al + 64, -16, None) == L.ZERO_EINVAL
+    assert cp(None, al, 16, None) == L.ZERO_EINVAL
+    assert cp(al + 8, al + 64, 16, None) == L.ZERO_EALIGN
+    assert cp(al, al + 16, 32, None) == L.ZERO_EINVAL               # overlapping
+    assert cp(al, al + 64, 1 << 60, None) == L.ZERO_ERANGE

@@ -1,0 +1,20 @@
+"""GPU: the reference copy used beside the nominal peak in the benchmark
+moves every byte unchanged."""
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 257, (1 << 24) + 48])
+def test_copy_reference_is_exact(nbytes):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import zero_sharded_mixed_partition_amd as Z
+    g = torch.Generator().manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes + 32,), dtype=torch.uint8, generator=g).cuda()
+    dst = torch.zeros(nbytes + 32, dtype=torch.uint8, device="cuda")
+    Z.zero_copy_reference(dst, src, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes])
+    assert int(dst[nbytes:].count_nonzero()) == 0          # nothing beyond the range is written

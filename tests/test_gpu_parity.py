@@ -99,7 +99,7 @@ def test_all_ranks_of_workload(Z, wname):
 
 # --------------------------------------------------------------------- sizes, tails, dtypes
 
-SIZES = [1, 3, 7, 8, 9, 255, 256, 257, 4099, 8192, 8192 + 8 * 1023 + 7, 256 * 2 * 8 * 3 + 5, 16384 * 5 + 3, 262144 + 8, 1_000_002, 8192 * 600 + 5]
+SIZES = [1, 3, 7, 8, 9, 255, 256, 257, 1023, 1024, 1025, 2049, 4099, 8192, 8192 + 8 * 1023 + 7, 256 * 2 * 8 * 3 + 5, 16384 * 5 + 3, 262144 + 8, 1_000_002, 8192 * 600 + 5]
 
 
 @pytest.mark.parametrize("n", SIZES)

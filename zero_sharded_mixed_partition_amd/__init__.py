@@ -294,6 +294,12 @@ class StepGraph:
             pass
 
 
+def zero_copy_reference(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
+    """Reference 16-byte-per-lane device copy of nbytes (default: all of src)."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _L.check(_L.lib().zero_copy_reference(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)), "zero_copy_reference")
+
+
 class LossScaler:
     """Host-side dynamic loss scale (C struct zero_loss_scaler)."""
 

@@ -56,6 +56,7 @@ SIGNATURES = {
     "zero_cpu_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
+    "zero_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "zero_status_string": (ctypes.c_char_p, [c_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }

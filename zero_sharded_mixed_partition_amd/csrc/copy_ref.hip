@@ -1,0 +1,53 @@
+// Reference device copy: the achievable streaming rate of one read stream
+// plus one write stream on this GPU, against which the step's kernels are
+// reported next to the nominal HBM peak.  It is a measurement aid, not a step
+// of the method.
+//
+// Each lane moves one 16-byte vector; a wave's load and store instructions
+// each cover one contiguous 1 KiB run.  One-shot grid of 256-thread
+// workgroups in address order; non-temporal hints on both sides, as in the
+// step's kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+#include "zero_shard.h"
+
+namespace zero_shard {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyThreads = 256;
+constexpr int64_t kCopyMaxGrid = (int64_t(1) << 31) - 1;
+
+__global__ __launch_bounds__(kCopyThreads) void copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       int64_t nvec) {
+    const int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (i < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+}  // namespace zero_shard
+
+using namespace zero_shard;
+
+extern "C" int zero_copy_reference(void* dst, const void* src, int64_t bytes, void* hip_stream) {
+    clear_error();
+    if (bytes < 0 || (bytes & 15)) return fail(ZERO_EINVAL, "bytes must be a non-negative multiple of 16");
+    if (bytes == 0) return ZERO_OK;
+    if (dst == nullptr || src == nullptr) return fail(ZERO_EINVAL, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u)
+        return fail(ZERO_EALIGN, "dst and src must be 16-byte aligned");
+    const int64_t nvec = bytes / 16;
+    const int64_t grid = (nvec + kCopyThreads - 1) / kCopyThreads;
+    if (grid > kCopyMaxGrid) return fail(ZERO_ERANGE, "copy too large for one launch");
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+    if (d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) return fail(ZERO_EINVAL, "dst and src overlap");
+    hipLaunchKernelGGL(copy16, dim3((unsigned)grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(hip_stream),
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZERO_EHIP, "copy16 launch: %s", hipGetErrorString(e));
+    return ZERO_OK;
+}

@@ -36,6 +36,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "zero_shard.h"
@@ -58,12 +60,20 @@ constexpr int64_t kNormChunk = (int64_t)kBlock * kNormUnroll;   // vectors per b
 // elementwise passes: one wave64 per workgroup, 4 consecutive elements per lane
 constexpr int kEwThreads = 64;
 constexpr int kEwTask = 4 * kEwThreads;                         // elements per workgroup per task
-// Occupancy cap.  With eight streams in flight HBM sustains more bytes per
-// second when fewer waves compete for DRAM rows: 12 KiB of LDS per
-// workgroup leaves room for 13 resident one-wave workgroups per CU (160 KiB
-// of LDS per CU on gfx950).  Chosen by measurement on MI355X over 0-32 KiB
-// (0 KiB: ~75% of HBM peak; 12 KiB: ~82%; 32 KiB: ~55%).
+// AdamW pass.  Each one-wave workgroup takes kAdamTasks consecutive tasks
+// and issues all their loads before any math; an LDS reservation that is
+// never read caps how many such workgroups are resident per CU (160 KiB of
+// LDS per CU on gfx950).  With eight streams in flight HBM sustains more bytes
+// per second when fewer waves compete for DRAM rows.  Chosen by measurement on
+// MI355X, a 976M-element shard stepped as in training (norm pass, update,
+// flag read): 1 task with 12 KiB (13 workgroups per CU) ~81.5% of HBM peak
+// (0 KiB ~75%, 32 KiB ~55%); 4 tasks at 5-6 workgroups per CU ~80%, at 8 or
+// 4 per CU 73-75%; 2 tasks ~79%.  Four tasks would make a skipped step 4x
+// cheaper (every workgroup reads the flag and exits: 0.2 instead of 0.8 ms on
+// that shard), but skipped steps are rare and applied ones are not.
 constexpr size_t kAdamLdsReserve = 12 * 1024;
+constexpr int kAdamTasks = 1;
+constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per workgroup
 // The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
 // peak with no reservation against 45-63% with the 12 KiB cap.
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
@@ -127,6 +137,16 @@ template <typename T>
 __device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
 template <typename T>
 __device__ __forceinline__ void st_stream(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), as straight-line code
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // the 4 gradient values of element group q (elements 4q .. 4q+3)
 template <int DT>
@@ -298,45 +318,87 @@ __device__ __forceinline__ void adam_body(float* __restrict__ P, float* __restri
         gscale = (float)(c.inv_scale * coef);
     }
     const int lane = threadIdx.x;
-    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
-    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
-        // lane owns elements [e0, e0 + 4): every access instruction of the wave
-        // covers one contiguous run (1 KiB per fp32 stream, 512 B per 16-bit one)
-        const int64_t e0 = t * kEwTask + 4 * lane;
-        if (e0 + 4 <= n) {
-            const int64_t q = e0 >> 2;
-            f32x4* p4 = reinterpret_cast<f32x4*>(P) + q;
-            f32x4* m4 = reinterpret_cast<f32x4*>(M) + q;
-            f32x4* v4 = reinterpret_cast<f32x4*>(V) + q;
-            f32x4 p = ld_stream(p4), m = ld_stream(m4), v = ld_stream(v4);
-            float g[4];
-            load_grad4<GDT>(G, q, g);
+    const int64_t ngroups = (n + kAdamGroup - 1) / kAdamGroup;
+    for (int64_t t = blockIdx.x; t < ngroups; t += gridDim.x) {
+        const int64_t base = t * kAdamGroup;
+        if (base + kAdamGroup <= n) {
+            // lane owns elements [4q, 4q + 4) of each task: every access
+            // instruction of the wave covers one contiguous run (1 KiB per
+            // fp32 stream, 512 B per 16-bit one)
+            f32x4 p[kAdamTasks], m[kAdamTasks], v[kAdamTasks];
+            float g[kAdamTasks][4];
+            // straight-line code per task (no loop): a loop whose store
+            // addresses become invariant gets its stores promoted by LICM,
+            // which drops their non-temporal hint
+            static_for<kAdamTasks>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int64_t q = (base >> 2) + k * kEwThreads + lane;
+                p[k] = ld_stream(reinterpret_cast<f32x4*>(P) + q);
+                m[k] = ld_stream(reinterpret_cast<f32x4*>(M) + q);
+                v[k] = ld_stream(reinterpret_cast<f32x4*>(V) + q);
+                load_grad4<GDT>(G, q, g[k]);
+            });
+            static_for<kAdamTasks>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int64_t q = (base >> 2) + k * kEwThreads + lane;
+                f32x4 po, mo, vo;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float pk = p[k], mk = m[k], vk = v[k];
-                adam_elem(c, gscale, g[k], pk, mk, vk);
-                p[k] = pk;
-                m[k] = mk;
-                v[k] = vk;
-            }
-            st_stream(p, p4);
-            st_stream(m, m4);
-            st_stream(v, v4);
-            if constexpr (WRITE_P) {
-                u32x2 out16;
-                out16[0] = to16<PDT>(p[0]) | (to16<PDT>(p[1]) << 16);
-                out16[1] = to16<PDT>(p[2]) | (to16<PDT>(p[3]) << 16);
-                st_stream(out16, reinterpret_cast<u32x2*>(Pout) + q);
-            }
-        } else if (e0 < n) {
-            // ragged tail: the last 1-3 elements, scalar accesses
-            for (int64_t e = e0; e < n; ++e) {
-                float p = P[e], m = M[e], v = V[e];
-                adam_elem(c, gscale, load_grad1<GDT>(G, e), p, m, v);
-                P[e] = p;
-                M[e] = m;
-                V[e] = v;
-                if constexpr (WRITE_P) Pout[e] = (uint16_t)to16<PDT>(p);
+                for (int j = 0; j < 4; ++j) {
+                    float pj = p[k][j], mj = m[k][j], vj = v[k][j];
+                    adam_elem(c, gscale, g[k][j], pj, mj, vj);
+                    po[j] = pj;
+                    mo[j] = mj;
+                    vo[j] = vj;
+                }
+                st_stream(po, reinterpret_cast<f32x4*>(P) + q);
+                st_stream(mo, reinterpret_cast<f32x4*>(M) + q);
+                st_stream(vo, reinterpret_cast<f32x4*>(V) + q);
+                if constexpr (WRITE_P) {
+                    u32x2 out16;
+                    out16[0] = to16<PDT>(po[0]) | (to16<PDT>(po[1]) << 16);
+                    out16[1] = to16<PDT>(po[2]) | (to16<PDT>(po[3]) << 16);
+                    st_stream(out16, reinterpret_cast<u32x2*>(Pout) + q);
+                }
+            });
+        } else {
+            // the last, partial group: whole vectors, then the 1-3 element
+            // ragged tail with scalar accesses
+            for (int64_t e0 = base + 4 * lane; e0 < n; e0 += kEwTask) {
+                if (e0 + 4 <= n) {
+                    const int64_t q = e0 >> 2;
+                    f32x4* p4 = reinterpret_cast<f32x4*>(P) + q;
+                    f32x4* m4 = reinterpret_cast<f32x4*>(M) + q;
+                    f32x4* v4 = reinterpret_cast<f32x4*>(V) + q;
+                    f32x4 pv = ld_stream(p4), mv = ld_stream(m4), vv = ld_stream(v4);
+                    float gv[4];
+                    load_grad4<GDT>(G, q, gv);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float pj = pv[j], mj = mv[j], vj = vv[j];
+                        adam_elem(c, gscale, gv[j], pj, mj, vj);
+                        pv[j] = pj;
+                        mv[j] = mj;
+                        vv[j] = vj;
+                    }
+                    st_stream(pv, p4);
+                    st_stream(mv, m4);
+                    st_stream(vv, v4);
+                    if constexpr (WRITE_P) {
+                        u32x2 out16;
+                        out16[0] = to16<PDT>(pv[0]) | (to16<PDT>(pv[1]) << 16);
+                        out16[1] = to16<PDT>(pv[2]) | (to16<PDT>(pv[3]) << 16);
+                        st_stream(out16, reinterpret_cast<u32x2*>(Pout) + q);
+                    }
+                } else {
+                    for (int64_t e = e0; e < n; ++e) {
+                        float pe = P[e], me = M[e], ve = V[e];
+                        adam_elem(c, gscale, load_grad1<GDT>(G, e), pe, me, ve);
+                        P[e] = pe;
+                        M[e] = me;
+                        V[e] = ve;
+                        if constexpr (WRITE_P) Pout[e] = (uint16_t)to16<PDT>(pe);
+                    }
+                }
             }
         }
     }
@@ -429,10 +491,10 @@ int launch_status(const char* what) {
 
 int grad_bytes(int32_t dt) { return dt == ZERO_F32 ? 4 : 2; }
 
-dim3 elementwise_grid(int64_t n) {
-    int64_t ntasks = (n + kEwTask - 1) / kEwTask;
-    if (ntasks > kEwMaxGrid) ntasks = kEwMaxGrid;   // the kernels stride over the rest
-    return dim3((unsigned)ntasks);
+dim3 elementwise_grid(int64_t n, int64_t per_group = kEwTask) {
+    int64_t ngroups = (n + per_group - 1) / per_group;
+    if (ngroups > kEwMaxGrid) ngroups = kEwMaxGrid;   // the kernels stride over the rest
+    return dim3((unsigned)ngroups);
 }
 
 template <int DT>
@@ -561,7 +623,7 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
     const int st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n,
                                    d_global_sqnorm, d_global_overflow);
     if (st != ZERO_OK || n == 0) return st;
-    launch_adam_any(grad_dtype, elementwise_grid(n), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
+    launch_adam_any(grad_dtype, elementwise_grid(n, kAdamGroup), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
                     param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, c, nullptr, d_global_sqnorm,
                     d_global_overflow);
     return launch_status("adam_update");
@@ -590,7 +652,7 @@ int zero_shard_adam_step_coef(float* master, float* exp_avg, float* exp_avg_sq, 
                                    d_global_sqnorm, d_global_overflow);
     if (st != ZERO_OK || n == 0) return st;
     const StepCoef unused{};
-    launch_adam_any(grad_dtype, elementwise_grid(n), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
+    launch_adam_any(grad_dtype, elementwise_grid(n, kAdamGroup), static_cast<hipStream_t>(hip_stream), param_out != nullptr,
                     param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, unused,
                     static_cast<const StepCoef*>(d_coef), d_global_sqnorm, d_global_overflow);
     return launch_status("adam_update_devcoef");
