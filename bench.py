@@ -79,10 +79,11 @@ def upload_inputs(w, begin, S, grad_dtype, block_chunks=16):
     return P, M, V, G
 
 
-def _oracle_block(w, lo, n, accum, threads=0):
+def _oracle_block(w, lo, n, accum, threads=0, reduce=0):
     """Seconds of oracle time for one full step (exact norm + AdamW; with
     `accum` > 0, that many micro-batch accumulations into the fp32 copy
-    first) on flat parameters [lo, lo+n); input generation excluded."""
+    first; with `reduce` > 0, the reduction of that many ranks' slices into
+    it) on flat parameters [lo, lo+n); input generation excluded."""
     import oracle
     import workloads as W
 
@@ -94,6 +95,9 @@ def _oracle_block(w, lo, n, accum, threads=0):
         for _ in range(accum):
             acc, _ovf = oracle.grad_accumulate(acc, g, w.grad_dtype, ginv)
         g, gfmt, ginv = acc, "f32", 1.0
+    elif reduce:
+        acc, _ovf = oracle.grad_reduce([g] * reduce, w.grad_dtype, ginv)
+        g, gfmt, ginv = acc, "f32", 1.0
     sq, ovf = oracle.shard_sqnorm_overflow(g, gfmt, ginv)
     oracle.shard_step(p, m, v, g, gfmt, w.param_dtype, global_sq=sq, global_overflow=ovf,
                       inv_loss_scale=ginv, max_grad_norm=w.max_grad_norm, lr=w.lr, beta1=w.beta1,
@@ -103,17 +107,17 @@ def _oracle_block(w, lo, n, accum, threads=0):
 
 def _oracle_worker(job):
     """One process of the all-cores leg: its blocks one after another, one thread."""
-    w, blocks, accum = job
+    w, blocks, accum, reduce = job
     if w.grad_dtype == "bf16":          # the bf16 input cast goes through torch's CPU kernels
         import torch
         torch.set_num_threads(1)
     spent = 0.0
     for lo, n in blocks:
-        spent += _oracle_block(w, lo, n, accum, threads=1)
+        spent += _oracle_block(w, lo, n, accum, threads=1, reduce=reduce)
     return sum(n for _, n in blocks), spent
 
 
-def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, max_procs=16):
+def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, max_procs=16, reduce=0):
     """The CPU oracle timed on a bounded sample of the same shard, blocks of
     consecutive parameters from its start, one step per block:
       all cores  one process per host core (at most `max_procs`), two blocks
@@ -127,7 +131,7 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1
     cores = max(1, min(max_procs, len(os.sched_getaffinity(0))))
     nblk = min(2 * cores, -(-S // par_block))
     blocks = [(begin + k * par_block, min(par_block, S - k * par_block)) for k in range(nblk)]
-    jobs = [(w, blocks[j::cores], accum) for j in range(cores) if blocks[j::cores]]
+    jobs = [(w, blocks[j::cores], accum, reduce) for j in range(cores) if blocks[j::cores]]
     with multiprocessing.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(_oracle_worker, jobs)
     par_done, par_time = sum(r[0] for r in res), max(r[1] for r in res)
@@ -135,9 +139,9 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1
     done, spent = 0, 0.0
     while spent < target_s and done < S:
         n = min(block, S - done)
-        spent += _oracle_block(w, begin + done, n, accum)
+        spent += _oracle_block(w, begin + done, n, accum, reduce=reduce)
         done += n
-    what = f"{accum} accumulations + " if accum else ""
+    what = f"{accum} accumulations + " if accum else f"reduction of {reduce} slices + " if reduce else ""
     return {"value": par_done / par_time, "unit": "params/s", "cores": len(jobs), "kind": "oracle",
             "sample": f"first {par_done} of the shard's {S} params in blocks of {par_block}, one step each "
                       f"({what}exact norm + AdamW, float64 NumPy), {len(jobs)} processes of one thread "
@@ -214,6 +218,9 @@ def main():
     ap.add_argument("--accum", type=int, default=0,
                     help="micro-batches accumulated into an fp32 gradient copy per step (0: step the 16-bit "
                          "gradient directly)")
+    ap.add_argument("--reduce", type=int, default=0,
+                    help="K: the step's gradient is the reduction of K ranks' 16-bit slices of this partition "
+                         "into the fp32 copy (the local half of the gradient reduce-scatter)")
     ap.add_argument("--offload", action="store_true",
                     help="keep the fp32 state in pinned host memory and step on host cores (CPU offload)")
     ap.add_argument("--graph", action="store_true",
@@ -221,9 +228,12 @@ def main():
                          "single launch; pays off on small shards where launches dominate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
-    if args.graph and (args.accum or args.offload):
-        print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum or "
-              "--offload", file=sys.stderr)
+    if args.graph and (args.accum or args.offload or args.reduce):
+        print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum, "
+              "--reduce or --offload", file=sys.stderr)
+        sys.exit(2)
+    if args.reduce and (args.accum or args.offload or not 1 <= args.reduce <= 16):
+        print("--reduce K takes 1 <= K <= 16 and does not combine with --accum or --offload", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on ONE GPU; --gpus {args.gpus} is not supported "
@@ -242,7 +252,7 @@ def main():
         # and its all-cores leg forks worker processes
         import oracle
         _, S0, _ = oracle.partition_plan(w.shapes, w.n_d, w.align)
-        cpu = cpu_baseline(w, w.rank * S0, S0, accum=args.accum)
+        cpu = cpu_baseline(w, w.rank * S0, S0, accum=args.accum, reduce=args.reduce)
         print(f"# cpu baseline {cpu['value']:.4g} params/s on {cpu['cores']} cores, "
               f"{cpu['one_core']['value']:.4g} on one", file=sys.stderr, flush=True)
 
@@ -261,7 +271,10 @@ def main():
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
                       applied_steps=w.step - 1, graph=args.graph)
     K = args.accum
-    A = torch.empty(S, dtype=torch.float32, device="cuda") if K else None
+    R = args.reduce
+    A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
+    # the other ranks' slices: copies of this rank's gradient (distinct buffers, same values)
+    slices = [G] + [G.clone() for _ in range(R - 1)] if R else None
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -274,7 +287,13 @@ def main():
                 opt.accumulate(A, G, first=(k == 0))
             if ev is not None:
                 ev[4].record()
-        grad = A if K else G
+        if R:
+            if ev is not None:
+                ev[3].record()
+            opt.reduce(A, slices)
+            if ev is not None:
+                ev[4].record()
+        grad = A if (K or R) else G
         if ev is not None:
             ev[0].record()
         opt.unscale_norm(grad)
@@ -328,14 +347,15 @@ def main():
     adam_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
-    adam_bpp = ADAM_F32_BYTES_PER_PARAM if K else ADAM_BYTES_PER_PARAM
-    norm_bpp = NORM_F32_BYTES_PER_PARAM if K else NORM_BYTES_PER_PARAM
+    adam_bpp = ADAM_F32_BYTES_PER_PARAM if (K or R) else ADAM_BYTES_PER_PARAM
+    norm_bpp = NORM_F32_BYTES_PER_PARAM if (K or R) else NORM_BYTES_PER_PARAM
     acc_bpp = (ACC_FIRST_BYTES_PER_PARAM + ACC_BYTES_PER_PARAM * (K - 1)) if K else 0
-    step_bpp = adam_bpp + norm_bpp + acc_bpp
+    red_bpp = 2 * R + 4 if R else 0
+    step_bpp = adam_bpp + norm_bpp + acc_bpp + red_bpp
     adam_avg = mean(adam_ms)
     adam_gbps = adam_bpp * S / (adam_avg * 1e-3) / 1e9
     step_gbps = step_bpp * S / (ms_step * 1e-3) / 1e9
-    run_key = w.name + (f"+accum{K}" if K else "") + ("+graph" if args.graph else "")
+    run_key = w.name + (f"+accum{K}" if K else "") + (f"+reduce{R}" if R else "") + ("+graph" if args.graph else "")
     traffic = measured_traffic(run_key)
     accum_stats = None
     if K:
@@ -344,6 +364,11 @@ def main():
                        "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
                        "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
                        "traffic": measured_traffic(run_key, "grad_accumulate")}
+    reduce_stats = None
+    if R:
+        red_ms = mean([e[3].elapsed_time(e[4]) for e in evs])
+        reduce_stats = {"slices": R, "kernel": "grad_reduce", "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
+                        "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9, "traffic": measured_traffic(run_key, "grad_reduce")}
 
     # the achievable rate of one read + one write stream over the same 14 B/param
     # each way (at most 16 GiB): the library's reference copy kernel, and
@@ -385,7 +410,8 @@ def main():
                    "flat_offset": begin, "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
                    "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
                    "weight_decay": w.weight_decay, "param_layout": w.param_layout,
-                   "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else "16-bit gradient")
+                   "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else
+                            f"reduction of {R} ranks' 16-bit slices into the fp32 copy" if R else "16-bit gradient")
                    + (", recorded step graph" if args.graph else ""),
                    "algorithmic_bytes_per_param": step_bpp},
         "hbm_gbps": step_gbps,
@@ -405,6 +431,7 @@ def main():
                            "frac_of_peak": ref_gbps / PEAK_HBM_GBPS, "adam_update_frac_of_copy": adam_gbps / ref_gbps,
                            "step_frac_of_copy": step_gbps / ref_gbps},
         "accumulate": accum_stats,
+        "reduce": reduce_stats,
         "torch_copy_gbps": copy_gbps,
         "skipped_steps": skipped,
         "cpu_baseline": cpu,

@@ -252,6 +252,36 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
                                void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Reduction of this partition's gradient over the data-parallel ranks: the
+ * local half of a gradient reduce-scatter.  Plain data parallelism sums the
+ * ranks' gradients (explainer, History, "Data parallelism's reign"); once
+ * gradients are partitioned each rank keeps the reduced gradient of its own
+ * partition only (explainer, Ch.02 "The Three Stages", what each stage shards,
+ * and the stage table: reduce-scatter).  A direct reduce-scatter delivers the
+ * K ranks' 16-bit gradients of this partition into K buffers on this GPU;
+ * this call sums them, in slice order, into the fp32 gradient copy:
+ *     acc = g_0 * inv,   then  acc = acc + g_k * inv  for k = 1 .. K-1,
+ * in fp32 with one rounding per addition (fused multiply-add): bit-identical
+ * to zero_shard_grad_accumulate over the slices in order.  A mean instead of
+ * a sum is inv_loss_scale / K.  The step then runs on acc (grad_dtype
+ * ZERO_F32), as after accumulation.
+ *
+ *  acc        device, [n] float32, written (not read); must not overlap a slice
+ *  slices     host array of n_slices device pointers, each [n] 16-bit
+ *             gradient of grad_dtype (ZERO_F16/ZERO_BF16), 16-byte aligned;
+ *             slices may alias one another
+ *  n_slices   K, 1 <= K <= ZERO_MAX_SLICES
+ *  inv_loss_scale  1 / loss scale (> 0, finite)
+ *  d_overflow device int32 or NULL: set to 1 if any slice holds an inf/NaN;
+ *             never cleared by the library
+ * Streams 2K + 4 bytes per element.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+#define ZERO_MAX_SLICES 16
+int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                           int64_t n, double inv_loss_scale, int32_t* d_overflow, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * The same step on host cores, for optimizer states kept in host memory (the
  * CPU-offload lineage: explainer, Legacy, "The trillion-parameter claim";
  * glossary description, CPU offloading).  All pointers are HOST pointers

@@ -196,6 +196,29 @@ def grad_accumulate(acc32: Optional[np.ndarray], grad_bits: np.ndarray, fmt: str
     return (base + t).astype(np.float32), bool(is_nonfinite16(grad_bits, fmt).any())
 
 
+def grad_reduce(slices, fmt: str, inv_loss_scale: float) -> Tuple[np.ndarray, bool]:
+    """The reduced gradient of this rank's partition over the data-parallel
+    ranks, from the ranks' 16-bit gradient slices of it, in rank order.
+
+    Plain data parallelism sums the ranks' gradients [Explainer, History,
+    "Data parallelism's reign"]; with gradients partitioned each rank keeps
+    only the reduced gradient of its own partition [Explainer, Ch.02 "The
+    Three Stages", what each stage shards; Ch.05 stage table: reduce-scatter].
+    Reading: the sum is formed slice by slice into the fp32 gradient copy,
+        acc <- float32(g_0 * inv),  acc <- float32(acc + g_k * inv),  k = 1..K-1,
+    each addition rounded once to float32: the fp32 copy accumulating the
+    ranks' slices as it accumulates micro-batches (grad_accumulate).
+    Returns (acc, overflow), overflow flagging an inf/NaN in any slice.
+    """
+    if len(slices) < 1:
+        raise ValueError("at least one slice")
+    acc, ovf = None, False
+    for g in slices:
+        acc, o = grad_accumulate(acc, g, fmt, inv_loss_scale)
+        ovf = ovf or o
+    return acc, ovf
+
+
 @dataclass(frozen=True)
 class LossScalerState:
     """Dynamic loss scale.  On an overflowing step: skip it, multiply the

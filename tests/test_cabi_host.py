@@ -235,3 +235,26 @@ def test_copy_reference_rejects_bad_arguments_on_host():
     assert cp(al + 8, al + 64, 16, None) == L.ZERO_EALIGN
     assert cp(al, al + 16, 32, None) == L.ZERO_EINVAL               # overlapping
     assert cp(al, al + 64, 1 << 60, None) == L.ZERO_ERANGE
+
+
+def test_reduce_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(1024)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    red = lib.zero_shard_grad_reduce
+
+    def ptrs(*a):
+        return (ctypes.c_void_p * len(a))(*a)
+
+    two = ptrs(al + 256, al + 512)
+    assert red(al, two, 2, L.ZERO_F16, 0, 1.0, None, None) == L.ZERO_OK             # n = 0: nothing launched
+    assert red(al, two, 0, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL
+    assert red(al, ptrs(*([al + 256] * 17)), 17, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL
+    assert red(al, two, 2, L.ZERO_F32, 8, 1.0, None, None) == L.ZERO_EINVAL         # 16-bit slices only
+    assert red(al, two, 2, L.ZERO_F16, -1, 1.0, None, None) == L.ZERO_EINVAL
+    assert red(al, two, 2, L.ZERO_F16, 8, 0.0, None, None) == L.ZERO_EINVAL
+    assert red(al, None, 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL
+    assert red(al, ptrs(al + 256, None), 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL
+    assert red(al, ptrs(al + 256, al + 520), 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EALIGN
+    assert red(al + 4, two, 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EALIGN
+    assert red(al, ptrs(al + 256, al + 16), 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL   # acc aliases

@@ -1,8 +1,8 @@
 """The streaming kernels' generated gfx950 code (no GPU needed: hipcc
 cross-compiles).
 
-Every 8- and 16-byte global load and store of the AdamW, accumulation and
-norm kernels must carry the non-temporal hint.  This is the layout the
+Every 8- and 16-byte global load and store of the AdamW, accumulation,
+reduction and norm kernels must carry the non-temporal hint.  This is the layout the
 kernels were measured in: a loop transformation in the compiler once
 promoted the AdamW stores out of a one-iteration loop and dropped the hint,
 costing about 10 points of HBM bandwidth without changing any result.  No
@@ -17,7 +17,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-STREAMING = ("adam_update", "adam_update_devcoef", "grad_accumulate", "sqnorm_partials")
+STREAMING = ("adam_update", "adam_update_devcoef", "grad_accumulate", "grad_reduce", "sqnorm_partials")
 
 
 @pytest.fixture(scope="module")

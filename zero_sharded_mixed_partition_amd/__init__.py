@@ -30,7 +30,8 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "zero_loss_scaler_update", "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZERO_F32",
            "ZeroShardError", "AdamHyper",
            "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam", "StepGraph", "zero_adam_coef_bytes",
-           "zero_adam_prepare", "zero_shard_adam_step_coef"]
+           "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
+           "MAX_SLICES"]
 
 
 def zero_abi_version() -> int:
@@ -167,6 +168,23 @@ def zero_shard_grad_accumulate(acc, grad, inv_loss_scale: float, first: bool, ov
 
 
 # ---------------------------------------------------------------- host-memory (offload) entry points
+
+MAX_SLICES = 16
+
+
+def zero_shard_grad_reduce(acc, slices, inv_loss_scale: float, overflow=None, grad_dtype: Optional[int] = None,
+                           n: Optional[int] = None, stream=None) -> None:
+    """acc = sum over slices (in order) of slice * inv_loss_scale, in fp32, one
+    rounding per addition; overflow (device int32) is set if any slice holds
+    an inf/NaN."""
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
+    gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
+    _L.check(_L.lib().zero_shard_grad_reduce(_ptr(acc), arr, len(slices), gd, n, float(inv_loss_scale),
+                                             _ptr(overflow), _stream(stream)), "zero_shard_grad_reduce")
+
 
 def _host_ptr(a) -> Optional[int]:
     """Address of a C-contiguous numpy array or CPU torch tensor."""

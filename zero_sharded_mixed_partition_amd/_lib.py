@@ -44,6 +44,7 @@ SIGNATURES = {
     "zero_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                      ctypes.POINTER(zero_adam_params), c_vp, c_vp, c_vp]),
     "zero_shard_grad_accumulate": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_dbl, c_i32, c_vp, c_vp]),
+    "zero_shard_grad_reduce": (c_i32, [c_vp, ctypes.POINTER(c_vp), c_i32, c_i32, c_i64, c_dbl, c_vp, c_vp]),
     "zero_adam_coef_bytes": (c_sz, []),
     "zero_adam_prepare": (c_i32, [ctypes.POINTER(zero_adam_params), c_vp]),
     "zero_shard_adam_step_coef": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64, c_vp, c_vp, c_vp, c_vp]),

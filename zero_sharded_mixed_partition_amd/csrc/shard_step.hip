@@ -474,6 +474,60 @@ __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict_
     if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
 }
 
+// ---------------------------------------------------------------- gradient reduction over ranks
+
+// The K ranks' 16-bit gradients of this partition, summed in slice order into
+// fp32 with one rounding per addition; the same operations, in the same
+// order, as K passes of grad_accumulate (first on slice 0).
+struct SlicePtrs {
+    const void* p[ZERO_MAX_SLICES];
+};
+
+template <int DT>
+__global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A, SlicePtrs sl, int k, int64_t n,
+                                                          float inv, int32_t* __restrict__ d_ovf) {
+    uint32_t bad = 0;
+    const int lane = threadIdx.x;
+    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
+    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
+        const int64_t e0 = t * kEwTask + 4 * lane;
+        if (e0 + 4 <= n) {
+            const int64_t q = e0 >> 2;
+            u32x2 w[ZERO_MAX_SLICES];
+            // every slice's load in flight before any math (k is uniform)
+#pragma unroll
+            for (int r = 0; r < ZERO_MAX_SLICES; ++r)
+                if (r < k) w[r] = ld_stream(static_cast<const u32x2*>(sl.p[r]) + q);
+            f32x4 a;
+#pragma unroll
+            for (int r = 0; r < ZERO_MAX_SLICES; ++r) {
+                if (r < k) {
+                    bad |= (w[r][0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                    bad |= (w[r][1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                    float g[4];
+                    unpack2<DT>(w[r][0], g[0], g[1]);
+                    unpack2<DT>(w[r][1], g[2], g[3]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[j] = r == 0 ? g[j] * inv : fmaf(g[j], inv, a[j]);
+                }
+            }
+            st_stream(a, reinterpret_cast<f32x4*>(A) + q);
+        } else if (e0 < n) {
+            for (int64_t e = e0; e < n; ++e) {
+                float a = 0.0f;
+                for (int r = 0; r < k; ++r) {
+                    const uint32_t h = static_cast<const uint16_t*>(sl.p[r])[e];
+                    bad |= (h & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                    const float g = load_grad1<DT>(sl.p[r], e);
+                    a = r == 0 ? g * inv : fmaf(g, inv, a);
+                }
+                A[e] = a;
+            }
+        }
+    }
+    if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
+}
+
 // ---------------------------------------------------------------- host helpers
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -686,6 +740,40 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
     }
 #undef ZS_ACC
     return launch_status("grad_accumulate");
+}
+
+int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n,
+                           double inv_loss_scale, int32_t* d_overflow, void* hip_stream) {
+    clear_error();
+    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
+    if (n_slices < 1 || n_slices > ZERO_MAX_SLICES)
+        return fail(ZERO_EINVAL, "n_slices must lie in [1, %d] (got %d)", ZERO_MAX_SLICES, n_slices);
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16 (got %d)", grad_dtype);
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    if (n == 0) return ZERO_OK;
+    if (acc == nullptr || slices == nullptr) return fail(ZERO_EINVAL, "NULL acc or slices");
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    if (!aligned16(acc)) return fail(ZERO_EALIGN, "acc must be 16-byte aligned");
+    if (d_overflow && ((uintptr_t)d_overflow & 3u)) return fail(ZERO_EALIGN, "d_overflow misaligned");
+    SlicePtrs sl{};
+    for (int32_t r = 0; r < n_slices; ++r) {
+        if (slices[r] == nullptr) return fail(ZERO_EINVAL, "slice %d is NULL", r);
+        if (!aligned16(slices[r])) return fail(ZERO_EALIGN, "slice %d must be 16-byte aligned", r);
+        if (overlaps(acc, n * 4, slices[r], n * 2)) return fail(ZERO_EINVAL, "acc aliases slice %d", r);
+        sl.p[r] = slices[r];
+    }
+    const dim3 grid = elementwise_grid(n);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const float inv = (float)inv_loss_scale;
+    if (grad_dtype == ZERO_F16)
+        hipLaunchKernelGGL(grad_reduce<ZERO_F16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
+                           d_overflow);
+    else
+        hipLaunchKernelGGL(grad_reduce<ZERO_BF16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
+                           d_overflow);
+    return launch_status("grad_reduce");
 }
 
 // ---------------------------------------------------------------- step graphs

@@ -15,7 +15,7 @@ import torch
 
 from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, dtype_code, zero_loss_scaler_update,
                zero_norm_workspace_bytes, zero_shard_adam_step, zero_shard_grad_accumulate,
-               zero_shard_unscale_norm_overflow)
+               zero_shard_grad_reduce, zero_shard_unscale_norm_overflow)
 
 
 class ShardAdam:
@@ -52,6 +52,12 @@ class ShardAdam:
         """Enqueue one micro-batch into the fp32 gradient copy `acc`
         (acc = (first ? 0 : acc) + grad / loss_scale)."""
         zero_shard_grad_accumulate(acc, grad, 1.0 / self.scaler.scale, first, overflow)
+
+    def reduce(self, acc: torch.Tensor, slices, overflow: Optional[torch.Tensor] = None) -> None:
+        """Enqueue the reduction of the data-parallel ranks' gradient slices of
+        this partition into the fp32 gradient copy `acc` (slice order,
+        acc = sum_k slice_k / loss_scale)."""
+        zero_shard_grad_reduce(acc, slices, 1.0 / self.scaler.scale, overflow)
 
     def unscale_norm(self, grad: torch.Tensor) -> None:
         """Enqueue steps 1-2: self.sqnorm, self.overflow <- this shard's values."""
