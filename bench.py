@@ -3,9 +3,12 @@
 one MI355X.
 
 A step is the whole hot path on this rank's shard, through the C ABI:
-  unscale + inf/NaN detection + squared norm (two kernels), the fused AdamW
-  update with clipping and 16-bit parameter writeback (one kernel), then the
-  4-byte overflow flag read back for the loss-scale / step-counter update.
+  unscale + inf/NaN detection + squared norm (two kernels; the second also
+  forms the step's coefficients and advances the loss scaler and step counter
+  kept in device memory), then the fused AdamW update with clipping and
+  16-bit parameter writeback (one kernel).  No step waits for the host.
+  --host-scaler instead reads the 4-byte overflow flag back every step and
+  updates the loss scale and step counter on the host.
 Inputs are seeded synthetic values uploaded to HBM before timing.
 
 Prints one JSON line.  `value` is params/s of the whole step; `roofline`
@@ -226,10 +229,13 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay one recorded step graph per step (norm pass, fused update and flag read as a "
                          "single launch; pays off on small shards where launches dominate)")
+    ap.add_argument("--host-scaler", action="store_true",
+                    help="keep the loss scaler and step counter on the host, reading the 4-byte overflow flag back "
+                         "every step (default: both live in device memory and no step waits for the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.graph and (args.accum or args.offload or args.reduce):
-        print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum, "
+        print("--graph records the host-scaled 16-bit-gradient step on the GPU; it does not combine with --accum, "
               "--reduce or --offload", file=sys.stderr)
         sys.exit(2)
     if args.reduce and (args.accum or args.offload or not 1 <= args.reduce <= 16):
@@ -269,7 +275,9 @@ def main():
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
-                      applied_steps=w.step - 1, graph=args.graph)
+                      applied_steps=w.step - 1, graph=args.graph,
+                      device_state=not (args.host_scaler or args.graph))
+    DS = opt.state is not None
     K = args.accum
     R = args.reduce
     A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
@@ -280,6 +288,8 @@ def main():
     def step(ev=None):
         if args.graph and ev is None:
             return opt.step(G, par)
+        if ev is not None:
+            ev[6].record()
         if K:
             for k in range(K):
                 if ev is not None and k == K - 1:
@@ -296,28 +306,42 @@ def main():
         grad = A if (K or R) else G
         if ev is not None:
             ev[0].record()
-        opt.unscale_norm(grad)
+        if DS:
+            opt.norm_decide(grad)              # the decision (coefficients, scaler, counts) in the norm's last kernel
+        else:
+            opt.unscale_norm(grad)
         if ev is not None:
             ev[1].record()
-        opt.apply(grad, par)
+            ev[5].record()
+        if DS:
+            opt.update(grad, par)
+        else:
+            opt.apply(grad, par)
         if ev is not None:
             ev[2].record()
-        return opt.finish()
+        return opt.finish()                    # device_state: None, nothing waits
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     skipped = 0
     wall = []
+    skipped0 = opt.read_state().skipped if DS else 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         ts = time.perf_counter()
-        skipped += step(None if args.graph else evs[k])      # ends with the flag read: the step is done
+        skipped += bool(step(None if args.graph else evs[k]))  # host scaler: ends with the flag read
         wall.append(time.perf_counter() - ts)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if DS:
+        # nothing waited inside the loop: per-step times from the events, start to next start
+        starts = [e[6] for e in evs]
+        wall = [starts[k].elapsed_time(starts[k + 1]) * 1e-3 for k in range(args.steps - 1)]
+        wall.append(starts[-1].elapsed_time(evs[-1][2]) * 1e-3)
+        skipped = opt.read_state().skipped - skipped0
     print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
     if args.graph:
         # a replayed graph has no events between its kernels: the per-kernel
@@ -332,19 +356,26 @@ def main():
     n_skip = min(10, args.steps)
     keep = G[S // 2].clone()
     G[S // 2] = float("inf")
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_skip)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_skip)]
+    skipped1 = opt.read_state().skipped if DS else 0
     torch.cuda.synchronize()
     skip_wall = []
     for k in range(n_skip):
         ts = time.perf_counter()
-        assert step(sev[k]), "a gradient holding +inf must skip the step"
+        r = step(sev[k])
+        if DS:
+            torch.cuda.synchronize()
+        else:
+            assert r, "a gradient holding +inf must skip the step"
         skip_wall.append(time.perf_counter() - ts)
+    if DS:
+        assert opt.read_state().skipped - skipped1 == n_skip, "a gradient holding +inf must skip the step"
     G[S // 2] = keep
     torch.cuda.synchronize()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    adam_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    adam_ms = sorted(e[5].elapsed_time(e[2]) for e in evs)
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
     adam_bpp = ADAM_F32_BYTES_PER_PARAM if (K or R) else ADAM_BYTES_PER_PARAM
@@ -412,11 +443,12 @@ def main():
                    "weight_decay": w.weight_decay, "param_layout": w.param_layout,
                    "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else
                             f"reduction of {R} ranks' 16-bit slices into the fp32 copy" if R else "16-bit gradient")
-                   + (", recorded step graph" if args.graph else ""),
+                   + (", recorded step graph" if args.graph else "")
+                   + (", scaler and step counter in device memory" if DS else ", host loss scaler (4-byte flag read per step)"),
                    "algorithmic_bytes_per_param": step_bpp},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
-        "roofline": {"bound": "hbm", "kernel": "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "adam_update_devcoef" if DS else "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": adam_bpp * S, "avg_ms": adam_avg,
                      "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9),
@@ -426,7 +458,7 @@ def main():
         "norm_pass": {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9},
         "skipped_step": {"steps": n_skip, "ms_per_step": mean(skip_wall) * 1e3,
                          "norm_ms": mean([e[0].elapsed_time(e[1]) for e in sev]),
-                         "update_ms": mean([e[1].elapsed_time(e[2]) for e in sev])},
+                         "update_ms": mean([e[5].elapsed_time(e[2]) for e in sev])},
         "copy_reference": {"kernel": "copy16 (zero_copy_reference)", "bytes_each_way": cbytes, "gbps": ref_gbps,
                            "frac_of_peak": ref_gbps / PEAK_HBM_GBPS, "adam_update_frac_of_copy": adam_gbps / ref_gbps,
                            "step_frac_of_copy": step_gbps / ref_gbps},

@@ -327,6 +327,80 @@ typedef struct {
 int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out);
 
 /* ---------------------------------------------------------------------------
+ * The step with its scalar state in device memory: no host round trip.
+ *
+ * The loss scaler and the step counts live in a zero_step_state in device
+ * memory.  The norm pass reads the loss scale from it; a one-thread kernel,
+ * enqueued by zero_shard_adam_step_dev after the global overflow flag is
+ * known, forms the coefficient block of step t = applied + 1 at that scale
+ * (the same routine as zero_adam_prepare, bit for bit) and then advances the
+ * state exactly as zero_loss_scaler_update does (skip: scale backed off,
+ * skipped + 1; otherwise applied + 1 and growth after growth_interval clean
+ * steps).  A whole step is therefore enqueued without waiting for the
+ * device; the host reads the state back only when it wants to.  Same
+ * passages as the norm pass, the update and the loss scaler above.
+ *
+ * zero_step_state: 72 bytes, device memory, 8-byte aligned, initialised by
+ * the caller (a valid scaler as for zero_loss_scaler_update; applied = the
+ * steps already applied; skipped, last_overflow, reserved = 0).
+ *
+ * zero_shard_unscale_norm_overflow_dev: zero_shard_unscale_norm_overflow
+ *   with inv_loss_scale = 1/scale read from d_state when the kernel runs
+ *   (1 for a ZERO_F32 gradient, which is already unscaled).
+ * zero_shard_norm_decide_dev: the norm pass of a single rank, whose flag is
+ *   the global one (no data-parallel reduction in between): its final
+ *   one-block kernel also makes the decision (as zero_step_decide_dev,
+ *   writing d_coef and advancing d_state); zero_shard_adam_step_coef with
+ *   d_coef follows.  Saves the decision kernel's launch.
+ * zero_step_decide_dev: the decision kernel alone: writes the coefficient
+ *   block to d_coef (device scratch of zero_adam_coef_bytes() bytes, 8-byte
+ *   aligned, owned by the caller) and advances d_state from
+ *   d_global_overflow.  grad_dtype ZERO_F32 (an already unscaled copy)
+ *   forms the block with inv_loss_scale 1.
+ * zero_shard_adam_step_dev: zero_step_decide_dev, then the fused update
+ *   (zero_shard_adam_step_coef with d_coef).  d_global_overflow is required;
+ *   d_global_sqnorm when clipping.  With n = 0 the state still advances.
+ * zero_shard_grad_accumulate_dev / zero_shard_grad_reduce_dev: the
+ *   accumulation and reduction with inv_loss_scale = 1/scale from d_state.
+ * In a data-parallel job every rank holds its own copy of the state; since
+ * all ranks see the same global overflow flag, the copies stay identical.
+ * Calls on one state must be ordered on one stream.
+ * Errors: as the host-scaled calls, plus ZERO_EINVAL / ZERO_EALIGN for the
+ * state pointer.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    double max_grad_norm;          /* <= 0 disables clipping */
+} zero_adam_hyper;
+
+typedef struct {
+    zero_loss_scaler scaler;
+    int64_t applied;               /* steps applied so far; the next step has t = applied + 1 */
+    int64_t skipped;               /* steps skipped on overflow so far */
+    int32_t last_overflow;         /* the last step's global overflow flag */
+    int32_t reserved;
+} zero_step_state;
+
+int zero_shard_unscale_norm_overflow_dev(const void* grad, int32_t grad_dtype, int64_t n,
+                                         const zero_step_state* d_state, double* d_sqnorm, int32_t* d_overflow,
+                                         void* d_workspace, size_t workspace_bytes, void* hip_stream);
+int zero_shard_norm_decide_dev(const void* grad, int32_t grad_dtype, int64_t n, const zero_adam_hyper* hp,
+                               zero_step_state* d_state, double* d_sqnorm, int32_t* d_overflow, void* d_coef,
+                               void* d_workspace, size_t workspace_bytes, void* hip_stream);
+int zero_step_decide_dev(const zero_adam_hyper* hp, int32_t grad_dtype, zero_step_state* d_state,
+                         const int32_t* d_global_overflow, void* d_coef, void* hip_stream);
+int zero_shard_adam_step_dev(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                             int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                             const zero_adam_hyper* hp, zero_step_state* d_state,
+                             const double* d_global_sqnorm, const int32_t* d_global_overflow, void* d_coef,
+                             void* hip_stream);
+int zero_shard_grad_accumulate_dev(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+                                   const zero_step_state* d_state, int32_t first, int32_t* d_overflow,
+                                   void* hip_stream);
+int zero_shard_grad_reduce_dev(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                               int64_t n, const zero_step_state* d_state, int32_t* d_overflow, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement aid (not a step of the method): a plain device copy, one
  * 16-byte vector per lane, in the same streaming style as the step's kernels.
  * Its rate is the achievable rate of one read plus one write stream, which

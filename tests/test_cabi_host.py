@@ -258,3 +258,88 @@ def test_reduce_rejects_bad_arguments_on_host():
     assert red(al, ptrs(al + 256, al + 520), 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EALIGN
     assert red(al + 4, two, 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EALIGN
     assert red(al, ptrs(al + 256, al + 16), 2, L.ZERO_F16, 8, 1.0, None, None) == L.ZERO_EINVAL   # acc aliases
+
+
+def test_device_state_calls_reject_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(1024)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    hp = L.zero_adam_hyper(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0)
+    bad = L.zero_adam_hyper(1e-3, 1.0, 0.999, 1e-8, 0.0, 1.0)
+    step = lib.zero_shard_adam_step_dev
+    args = (al, al + 64, al + 128, al + 192, L.ZERO_F16, None, 0, 4)
+    assert step(*args, ctypes.byref(hp), None, al + 256, al + 264, al + 320, None) == L.ZERO_EINVAL        # state
+    assert step(*args, ctypes.byref(hp), al + 4, al + 256, al + 264, al + 320, None) == L.ZERO_EALIGN      # state
+    assert step(*args, ctypes.byref(hp), al + 512, al + 256, None, al + 320, None) == L.ZERO_EINVAL        # flag
+    assert step(*args, ctypes.byref(hp), al + 512, None, al + 264, al + 320, None) == L.ZERO_EINVAL        # clip
+    assert step(*args, ctypes.byref(hp), al + 512, al + 256, al + 264, None, None) == L.ZERO_EINVAL        # coef
+    assert step(*args, ctypes.byref(bad), al + 512, al + 256, al + 264, al + 320, None) == L.ZERO_EINVAL   # beta
+    assert step(*args, None, al + 512, al + 256, al + 264, al + 320, None) == L.ZERO_EINVAL
+    norm = lib.zero_shard_unscale_norm_overflow_dev
+    assert norm(al, L.ZERO_F16, 8, None, al + 256, al + 264, al + 320, 1024, None) == L.ZERO_EINVAL
+    assert norm(al, L.ZERO_F16, 8, al + 2, al + 256, al + 264, al + 320, 1024, None) == L.ZERO_EALIGN
+    acc = lib.zero_shard_grad_accumulate_dev
+    assert acc(al, al + 256, L.ZERO_F16, 8, None, 1, None, None) == L.ZERO_EINVAL
+    red = lib.zero_shard_grad_reduce_dev
+    two = (ctypes.c_void_p * 2)(al + 256, al + 512)
+    assert red(al, two, 2, L.ZERO_F16, 8, None, None, None) == L.ZERO_EINVAL
+
+
+def test_coefficients_use_binary_exponentiation():
+    """beta^t is taken by binary exponentiation in float64 (the same IEEE
+    multiplications on host and device); over a sweep the block equals that
+    formula bit for bit, and differs from a library pow by at most one float32
+    rounding boundary (never observed in the sweep)."""
+    import struct
+
+    import numpy as np
+
+    def pow_int(b, e):
+        r = 1.0
+        while e > 0:
+            if e & 1:
+                r = r * b
+            b = b * b
+            e >>= 1
+        return r
+
+    f32 = lambda x: float(np.float32(x))  # noqa: E731
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        b1, b2 = float(rng.uniform(0, 0.9999)), float(rng.uniform(0, 0.99999))
+        t = int(rng.integers(1, 10**6))
+        lr = float(rng.uniform(1e-5, 1e-2))
+        buf = np.zeros(Z.zero_adam_coef_bytes(), np.uint8)
+        Z.zero_adam_prepare(Z.AdamHyper(lr=lr, beta1=b1, beta2=b2, eps=1e-8, weight_decay=0.0, step=t,
+                                        inv_loss_scale=1.0, max_grad_norm=0.0), buf)
+        got = struct.unpack("<9fi2d", buf.tobytes())
+        assert got[4] == f32(lr / (1 - pow_int(b1, t)))
+        assert got[5] == f32(1 / (1 - pow_int(b2, t)) ** 0.5)
+        assert got[4] == f32(lr / (1 - b1 ** t)) and got[5] == f32(1 / (1 - b2 ** t) ** 0.5)
+
+
+def test_decide_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(1024)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    hp = L.zero_adam_hyper(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0)
+    dec = lib.zero_step_decide_dev
+    assert dec(None, L.ZERO_F16, al, al + 256, al + 320, None) == L.ZERO_EINVAL
+    assert dec(ctypes.byref(hp), 7, al, al + 256, al + 320, None) == L.ZERO_EINVAL
+    assert dec(ctypes.byref(hp), L.ZERO_F16, None, al + 256, al + 320, None) == L.ZERO_EINVAL
+    assert dec(ctypes.byref(hp), L.ZERO_F16, al, None, al + 320, None) == L.ZERO_EINVAL
+    assert dec(ctypes.byref(hp), L.ZERO_F16, al, al + 257, al + 320, None) == L.ZERO_EINVAL
+    assert dec(ctypes.byref(hp), L.ZERO_F16, al, al + 256, al + 324, None) == L.ZERO_EINVAL
+
+
+def test_norm_decide_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(1024)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    hp = L.zero_adam_hyper(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0)
+    nd = lib.zero_shard_norm_decide_dev
+    assert nd(al, L.ZERO_F16, 8, None, al + 512, al + 256, al + 264, al + 320, al + 384, 1024, None) == L.ZERO_EINVAL
+    assert nd(al, L.ZERO_F16, 8, ctypes.byref(hp), None, al + 256, al + 264, al + 320, al + 384, 1024, None) == L.ZERO_EINVAL
+    assert nd(al, L.ZERO_F16, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, None, al + 384, 1024, None) == L.ZERO_EINVAL
+    assert nd(al, 7, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, al + 320, al + 384, 1024, None) == L.ZERO_EINVAL
+    assert nd(al, L.ZERO_F16, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, al + 320, al + 384, 0, None) == L.ZERO_ENOSPC

@@ -21,8 +21,8 @@ import ctypes
 from typing import List, Optional, Sequence, Tuple
 
 from . import _lib as _L
-from ._lib import (ZERO_BF16, ZERO_F16, ZERO_F32, ZeroShardError, zero_adam_params,  # noqa: F401
-                   zero_fragment, zero_loss_scaler)
+from ._lib import (ZERO_BF16, ZERO_F16, ZERO_F32, ZeroShardError, zero_adam_hyper,  # noqa: F401
+                   zero_adam_params, zero_fragment, zero_loss_scaler, zero_step_state)
 
 __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_bytes",
            "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_shard_grad_accumulate",
@@ -31,7 +31,9 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "ZeroShardError", "AdamHyper",
            "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam", "StepGraph", "zero_adam_coef_bytes",
            "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
-           "MAX_SLICES"]
+           "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
+           "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
+           "zero_shard_norm_decide_dev"]
 
 
 def zero_abi_version() -> int:
@@ -316,6 +318,95 @@ def zero_copy_reference(dst, src, nbytes: Optional[int] = None, stream=None) -> 
     """Reference 16-byte-per-lane device copy of nbytes (default: all of src)."""
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _L.check(_L.lib().zero_copy_reference(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)), "zero_copy_reference")
+
+
+class StepState:
+    """The loss scaler and step counts in device memory (C struct
+    zero_step_state), for the calls that keep a whole step on the device."""
+
+    def __init__(self, scaler: "LossScaler", applied_steps: int = 0, device=None):
+        import torch
+        host = zero_step_state(scaler.s, int(applied_steps), 0, 0, 0)
+        raw = bytes(host)
+        self.tensor = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(device or "cuda")
+
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+    def read(self) -> zero_step_state:
+        """Copy the state to the host (synchronises with its stream)."""
+        raw = bytes(self.tensor.cpu().numpy().tobytes())
+        return zero_step_state.from_buffer_copy(raw)
+
+
+def _hyper(hp: "AdamHyper") -> zero_adam_hyper:
+    p = hp.c()
+    return zero_adam_hyper(p.lr, p.beta1, p.beta2, p.eps, p.weight_decay, p.max_grad_norm)
+
+
+def zero_shard_unscale_norm_overflow_dev(grad, state: StepState, sqnorm, overflow, workspace,
+                                         grad_dtype: Optional[int] = None, n: Optional[int] = None,
+                                         stream=None) -> None:
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = grad.numel() if n is None else n
+    _L.check(_L.lib().zero_shard_unscale_norm_overflow_dev(_ptr(grad), gd, n, state.ptr(), _ptr(sqnorm),
+                                                           _ptr(overflow), _ptr(workspace),
+                                                           workspace.numel() * workspace.element_size(),
+                                                           _stream(stream)), "zero_shard_unscale_norm_overflow_dev")
+
+
+def zero_shard_adam_step_dev(master, exp_avg, exp_avg_sq, grad, param_out, hp: "AdamHyper", state: StepState,
+                             global_sqnorm, global_overflow, d_coef, grad_dtype: Optional[int] = None,
+                             param_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """hp.step and hp.inv_loss_scale are ignored: t and the scale come from the device state."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
+    n = master.numel() if n is None else n
+    h = _hyper(hp)
+    _L.check(_L.lib().zero_shard_adam_step_dev(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
+                                               _ptr(param_out), pd, n, ctypes.byref(h), state.ptr(),
+                                               _ptr(global_sqnorm), _ptr(global_overflow), _ptr(d_coef),
+                                               _stream(stream)), "zero_shard_adam_step_dev")
+
+
+def zero_shard_norm_decide_dev(grad, hp: "AdamHyper", state: StepState, sqnorm, overflow, d_coef, workspace,
+                               grad_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """Single-rank norm pass whose final kernel also makes the step's decision."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = grad.numel() if n is None else n
+    h = _hyper(hp)
+    _L.check(_L.lib().zero_shard_norm_decide_dev(_ptr(grad), gd, n, ctypes.byref(h), state.ptr(), _ptr(sqnorm),
+                                                 _ptr(overflow), _ptr(d_coef), _ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+             "zero_shard_norm_decide_dev")
+
+
+def zero_step_decide_dev(hp: "AdamHyper", grad_dtype, state: StepState, global_overflow, d_coef,
+                         stream=None) -> None:
+    """The decision kernel: d_coef <- coefficients of step applied+1, state advanced by the flag."""
+    h = _hyper(hp)
+    _L.check(_L.lib().zero_step_decide_dev(ctypes.byref(h), dtype_code(grad_dtype), state.ptr(),
+                                           _ptr(global_overflow), _ptr(d_coef), _stream(stream)),
+             "zero_step_decide_dev")
+
+
+def zero_shard_grad_accumulate_dev(acc, grad, state: StepState, first: bool, overflow=None,
+                                   grad_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    _L.check(_L.lib().zero_shard_grad_accumulate_dev(_ptr(acc), _ptr(grad), gd, n, state.ptr(), 1 if first else 0,
+                                                     _ptr(overflow), _stream(stream)), "zero_shard_grad_accumulate_dev")
+
+
+def zero_shard_grad_reduce_dev(acc, slices, state: StepState, overflow=None, grad_dtype: Optional[int] = None,
+                               n: Optional[int] = None, stream=None) -> None:
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
+    gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
+    _L.check(_L.lib().zero_shard_grad_reduce_dev(_ptr(acc), arr, len(slices), gd, n, state.ptr(), _ptr(overflow),
+                                                 _stream(stream)), "zero_shard_grad_reduce_dev")
 
 
 class LossScaler:

@@ -33,6 +33,16 @@ class zero_loss_scaler(ctypes.Structure):
                 ("growth_interval", c_i64), ("good_steps", c_i64)]
 
 
+class zero_adam_hyper(ctypes.Structure):
+    _fields_ = [("lr", c_dbl), ("beta1", c_dbl), ("beta2", c_dbl), ("eps", c_dbl), ("weight_decay", c_dbl),
+                ("max_grad_norm", c_dbl)]
+
+
+class zero_step_state(ctypes.Structure):
+    _fields_ = [("scaler", zero_loss_scaler), ("applied", c_i64), ("skipped", c_i64), ("last_overflow", c_i32),
+                ("reserved", c_i32)]
+
+
 # name -> (restype, argtypes); every symbol the header declares
 SIGNATURES = {
     "zero_abi_version": (c_i32, []),
@@ -58,6 +68,14 @@ SIGNATURES = {
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
     "zero_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
+    "zero_shard_unscale_norm_overflow_dev": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "zero_shard_norm_decide_dev": (c_i32, [c_vp, c_i32, c_i64, ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_sz, c_vp]),
+    "zero_step_decide_dev": (c_i32, [ctypes.POINTER(zero_adam_hyper), c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "zero_shard_adam_step_dev": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
+                                         ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "zero_shard_grad_accumulate_dev": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_vp, c_i32, c_vp, c_vp]),
+    "zero_shard_grad_reduce_dev": (c_i32, [c_vp, ctypes.POINTER(c_vp), c_i32, c_i32, c_i64, c_vp, c_vp, c_vp]),
     "zero_status_string": (ctypes.c_char_p, [c_i32]),
     "zero_last_error": (ctypes.c_char_p, []),
 }

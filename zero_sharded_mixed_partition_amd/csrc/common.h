@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdint>
 
+#include "step_coef.h"
 #include "zero_shard.h"
 
 namespace zero_shard {
@@ -12,21 +13,11 @@ namespace zero_shard {
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// Per-step AdamW coefficients, derived on the host in double from the
-// hyperparameters and rounded once each to float (shared by the device and
-// the host implementations of the step).
-struct StepCoef {
-    float beta1, omb1, beta2, omb2;   // beta, 1 - beta
-    float step_size;                  // lr / (1 - beta1^t)
-    float rsqrt_bc2;                  // 1 / sqrt(1 - beta2^t)
-    float eps;
-    float decay;                      // 1 - lr * wd
-    float gscale_fixed;               // float(inv_scale), the gradient factor when clipping is off
-    int clip;                         // max_grad_norm > 0
-    double inv_scale, max_norm;
-};
-
-// Validates hp and fills c; returns ZERO_OK or an error status (with detail).
+// Validates hp and fills c (fill_step_coef); returns ZERO_OK or an error
+// status (with detail).
 int prepare_adam(const zero_adam_params* hp, StepCoef* c);
+
+// Validates the step-independent hyperparameters (no t, no loss scale).
+int check_hyper(double lr, double beta1, double beta2, double eps, double weight_decay, double max_grad_norm);
 
 }  // namespace zero_shard

@@ -29,37 +29,30 @@ int fail(int status, const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
+int check_hyper(double lr, double beta1, double beta2, double eps, double weight_decay, double max_grad_norm) {
+    if (!(lr >= 0.0) || !std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite and >= 0");
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+        return fail(ZERO_EINVAL, "betas must lie in [0, 1)");
+    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
+    if (!(weight_decay >= 0.0) || !std::isfinite(weight_decay))
+        return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
+    if (max_grad_norm > 0.0 && !std::isfinite(max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm must be finite");
+    if (std::isnan(max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm is NaN");
+    return ZERO_OK;
+}
+
 int prepare_adam(const zero_adam_params* hp, StepCoef* c) {
     if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
     const zero_adam_params& h = *hp;
-    if (!(h.lr >= 0.0) || !std::isfinite(h.lr)) return fail(ZERO_EINVAL, "lr must be finite and >= 0");
-    if (!(h.beta1 >= 0.0 && h.beta1 < 1.0) || !(h.beta2 >= 0.0 && h.beta2 < 1.0))
-        return fail(ZERO_EINVAL, "betas must lie in [0, 1)");
-    if (!(h.eps >= 0.0) || !std::isfinite(h.eps)) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
-    if (!(h.weight_decay >= 0.0) || !std::isfinite(h.weight_decay))
-        return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
+    const int st = check_hyper(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.max_grad_norm);
+    if (st != ZERO_OK) return st;
     if (h.step < 1) return fail(ZERO_EINVAL, "step (1-based index of the step applied) must be >= 1");
     if (!(h.inv_loss_scale > 0.0) || !std::isfinite(h.inv_loss_scale))
         return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
-    const bool clip = h.max_grad_norm > 0.0;
-    if (clip && !std::isfinite(h.max_grad_norm)) return fail(ZERO_EINVAL, "max_grad_norm must be finite");
     // bias corrections of the step being applied (Adam, 1-based t)
-    const double t = (double)h.step;
-    const double bc1 = 1.0 - std::pow(h.beta1, t);
-    const double bc2 = 1.0 - std::pow(h.beta2, t);
-    if (!(bc1 > 0.0) || !(bc2 > 0.0)) return fail(ZERO_ERANGE, "bias correction underflows to 0");
-    c->beta1 = (float)h.beta1;
-    c->omb1 = (float)(1.0 - h.beta1);
-    c->beta2 = (float)h.beta2;
-    c->omb2 = (float)(1.0 - h.beta2);
-    c->step_size = (float)(h.lr / bc1);
-    c->rsqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
-    c->eps = (float)h.eps;
-    c->decay = (float)(1.0 - h.lr * h.weight_decay);
-    c->gscale_fixed = (float)h.inv_loss_scale;
-    c->clip = clip ? 1 : 0;
-    c->inv_scale = h.inv_loss_scale;
-    c->max_norm = clip ? h.max_grad_norm : 0.0;
+    if (!(bias_correction(h.beta1, h.step) > 0.0) || !(bias_correction(h.beta2, h.step) > 0.0))
+        return fail(ZERO_ERANGE, "bias correction underflows to 0");
+    fill_step_coef(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step, h.inv_loss_scale, h.max_grad_norm, c);
     return ZERO_OK;
 }
 

@@ -55,8 +55,9 @@ constexpr int kWaves = kBlock / 64;
 // grid-stride loop reads a 16 KiB chunk per block.  Chosen by measurement on
 // MI355X (~7.1 TB/s on a 2 GB gradient shard).
 constexpr int kNormMaxBlocks = 512;
-constexpr int kNormUnroll = 4;                                  // 16-byte loads in flight per thread
-constexpr int64_t kNormChunk = (int64_t)kBlock * kNormUnroll;   // vectors per block per step
+// 16-byte loads in flight per thread: 4 for a 16-bit gradient, 8 for an fp32
+// one (fp32: 7.1 TB/s with 8 against 6.5 with 4 on a 3.9 GB gradient; 16-bit:
+// 4 is best at 0.5 and 2 GB), so a block step covers 8K elements either way.
 // elementwise passes: one wave64 per workgroup, 4 consecutive elements per lane
 constexpr int kEwThreads = 64;
 constexpr int kEwTask = 4 * kEwThreads;                         // elements per workgroup per task
@@ -91,16 +92,19 @@ struct GradFmt;
 template <>
 struct GradFmt<ZERO_F16> {
     static constexpr int per_vec = 8;
+    static constexpr int norm_unroll = 4;
     static constexpr uint32_t mask = 0x7C007C00u, carry = 0x04000400u;
 };
 template <>
 struct GradFmt<ZERO_BF16> {
     static constexpr int per_vec = 8;
+    static constexpr int norm_unroll = 4;
     static constexpr uint32_t mask = 0x7F807F80u, carry = 0x00800080u;
 };
 template <>
 struct GradFmt<ZERO_F32> {
     static constexpr int per_vec = 4;
+    static constexpr int norm_unroll = 8;
     static constexpr uint32_t mask = 0x7F800000u, carry = 0x00800000u;
 };
 constexpr uint32_t kNonfiniteBits = 0x80008000u;
@@ -219,7 +223,7 @@ __device__ __forceinline__ void accumulate_vec(u32x4 q, double& acc, uint32_t& b
     }
 }
 
-// Grid-stride over chunks of kNormChunk consecutive 16-byte vectors: at every
+// Grid-stride over chunks of kChunk consecutive 16-byte vectors: at every
 // step the grid reads one contiguous window, and each wave's four loads are
 // consecutive 1 KiB runs.  The grid size depends only on n, so the summation
 // order (and the result) is the same on every run.
@@ -232,18 +236,20 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restric
     __shared__ uint32_t s_bad[kWaves];
     double acc = 0.0;
     uint32_t bad = 0;
-    const int64_t nchunks = nvec / kNormChunk;
+    constexpr int kUnroll = GradFmt<DT>::norm_unroll;
+    constexpr int64_t kChunk = (int64_t)kBlock * kUnroll;
+    const int64_t nchunks = nvec / kChunk;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const u32x4* base = g + c * kNormChunk + threadIdx.x;
-        u32x4 q[kNormUnroll];
+        const u32x4* base = g + c * kChunk + threadIdx.x;
+        u32x4 q[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kNormUnroll; ++u) q[u] = ld_stream(base + u * kBlock);
+        for (int u = 0; u < kUnroll; ++u) q[u] = ld_stream(base + u * kBlock);
 #pragma unroll
-        for (int u = 0; u < kNormUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
+        for (int u = 0; u < kUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
     }
     if (blockIdx.x == 0) {
-        // fewer than kNormChunk vectors left over, then less than one vector
-        for (int64_t i = nchunks * kNormChunk + threadIdx.x; i < nvec; i += kBlock)
+        // fewer than kChunk vectors left over, then less than one vector
+        for (int64_t i = nchunks * kChunk + threadIdx.x; i < nvec; i += kBlock)
             accumulate_vec<DT>(ld_stream(g + i), acc, bad);
         if (threadIdx.x == 0) {
             for (int k = 0; k < tail_n; ++k) {
@@ -264,11 +270,57 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restric
     }
 }
 
+// ---------------------------------------------------------------- device-resident step state
+
+struct HyperArgs {
+    double lr, beta1, beta2, eps, weight_decay, max_grad_norm;
+};
+
+// After the (global) overflow flag is known: the coefficient block of step
+// t = applied + 1 at the current loss scale, then the loss scale and the step
+// counts advanced exactly as zero_loss_scaler_update does on the host.  The
+// update kernel that follows reads the block and the flag.  One thread.
+__device__ void decide_step(zero_step_state* __restrict__ st, int32_t ovf, const HyperArgs& h, int unscaled_grad,
+                            StepCoef* __restrict__ coef) {
+    zero_loss_scaler s = st->scaler;
+    const double inv = unscaled_grad ? 1.0 : 1.0 / s.scale;
+    StepCoef c;
+    fill_step_coef(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, st->applied + 1, inv, h.max_grad_norm, &c);
+    *coef = c;
+    if (ovf) {
+        const double next = s.scale * s.backoff;
+        s.scale = next > s.min_scale ? next : s.min_scale;
+        s.good_steps = 0;
+        st->skipped += 1;
+    } else {
+        st->applied += 1;
+        s.good_steps += 1;
+        if (s.good_steps >= s.growth_interval) {
+            s.scale *= s.growth;
+            s.good_steps = 0;
+        }
+    }
+    st->scaler = s;
+    st->last_overflow = ovf;
+}
+
+__global__ __launch_bounds__(64) void step_decide(zero_step_state* __restrict__ st, const int32_t* __restrict__ d_ovf,
+                                                  HyperArgs h, int unscaled_grad, StepCoef* __restrict__ coef) {
+    if (threadIdx.x == 0) decide_step(st, *d_ovf != 0 ? 1 : 0, h, unscaled_grad, coef);
+}
+
+// d_scale (device loss scale) or, if NULL, inv2 by value: the factor applied
+// to the raw sum of squares is (1/scale)^2.
+// With st_decide set (a single rank, whose flag is the global one), thread 0
+// also makes the step's decision (decide_step) from the flag it just formed.
 __global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restrict__ part_sq,
                                                           const uint32_t* __restrict__ part_bad,
                                                           int nparts, double inv2,
+                                                          const double* __restrict__ d_scale,
                                                           double* __restrict__ d_sq,
-                                                          int32_t* __restrict__ d_ovf) {
+                                                          int32_t* __restrict__ d_ovf,
+                                                          zero_step_state* __restrict__ st_decide, HyperArgs h,
+                                                          int unscaled_grad, StepCoef* __restrict__ coef) {
     __shared__ double s_sq[kWaves];
     __shared__ uint32_t s_bad[kWaves];
     double acc = 0.0;
@@ -279,14 +331,21 @@ __global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restri
     }
     block_reduce(acc, bad, s_sq, s_bad);
     if (threadIdx.x == 0) {
+        if (d_scale != nullptr) {
+            const double inv = 1.0 / *d_scale;
+            inv2 = inv * inv;
+        }
         *d_sq = acc * inv2;
         *d_ovf = bad ? 1 : 0;
+        if (st_decide != nullptr) decide_step(st_decide, bad ? 1 : 0, h, unscaled_grad, coef);
     }
 }
 
-// blocks for a gradient of nvec 16-byte vectors: one per full chunk, at most kNormMaxBlocks
-int norm_blocks(int64_t nvec) {
-    int64_t b = nvec / kNormChunk;
+// blocks for a gradient of n elements: one per full block step (8K elements
+// in every format), at most kNormMaxBlocks
+constexpr int64_t kNormChunkElems = 8192;
+int norm_blocks(int64_t n) {
+    int64_t b = n / kNormChunkElems;
     if (b < 1) b = 1;
     if (b > kNormMaxBlocks) b = kNormMaxBlocks;
     return (int)b;
@@ -437,7 +496,9 @@ __global__ __launch_bounds__(kEwThreads) void adam_update_devcoef(float* __restr
 template <int DT, bool FIRST>
 __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict__ A, const void* __restrict__ G,
                                                               int64_t n, float inv,
+                                                              const double* __restrict__ d_scale,
                                                               int32_t* __restrict__ d_ovf) {
+    if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     uint32_t bad = 0;
     const int lane = threadIdx.x;
     const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
@@ -485,7 +546,9 @@ struct SlicePtrs {
 
 template <int DT>
 __global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A, SlicePtrs sl, int k, int64_t n,
-                                                          float inv, int32_t* __restrict__ d_ovf) {
+                                                          float inv, const double* __restrict__ d_scale,
+                                                          int32_t* __restrict__ d_ovf) {
+    if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     uint32_t bad = 0;
     const int lane = threadIdx.x;
     const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
@@ -626,20 +689,23 @@ extern "C" {
 
 size_t zero_norm_workspace_bytes(int64_t n) {
     if (n < 0) return 0;
-    // sized for the format with the most 16-byte vectors (fp32: 4 per vector)
-    const size_t b = (size_t)norm_blocks((n + 3) / 4);
+    // one (double, uint32) partial per norm block; the block count depends on n only
+    const size_t b = (size_t)norm_blocks(n);
     return ((b * (sizeof(double) + sizeof(uint32_t))) + 255) & ~(size_t)255;
 }
 
-int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
-                                     double* d_sqnorm, int32_t* d_overflow, void* d_workspace,
-                                     size_t workspace_bytes, void* hip_stream) {
-    clear_error();
+}  // extern "C"
+
+namespace zero_shard {
+namespace {
+
+// The norm pass; the (1/scale)^2 factor is inv2 by value, or read from d_scale.
+int norm_pass(const void* grad, int32_t grad_dtype, int64_t n, double inv2, const double* d_scale, double* d_sqnorm,
+              int32_t* d_overflow, void* d_workspace, size_t workspace_bytes, hipStream_t s,
+              zero_step_state* st_decide = nullptr, const HyperArgs& h = HyperArgs{}, StepCoef* coef = nullptr) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
     if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
         return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
-    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
-        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
     if (d_sqnorm == nullptr || d_overflow == nullptr || d_workspace == nullptr)
         return fail(ZERO_EINVAL, "NULL output or workspace pointer");
     if (n > 0 && grad == nullptr) return fail(ZERO_EINVAL, "grad is NULL");
@@ -649,9 +715,7 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
         return fail(ZERO_EALIGN, "d_sqnorm / d_overflow misaligned");
     if (workspace_bytes < zero_norm_workspace_bytes(n))
         return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, zero_norm_workspace_bytes(n));
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const int64_t per_vec = grad_dtype == ZERO_F32 ? 4 : 8;
-    const int nb = norm_blocks(n / per_vec);
+    const int nb = norm_blocks(n);
     double* part_sq = static_cast<double*>(d_workspace);
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + nb);
     if (n > 0) {
@@ -661,9 +725,42 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
         const int st = launch_status("sqnorm_partials");
         if (st != ZERO_OK) return st;
     }
-    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, n > 0 ? nb : 0,
-                       inv_loss_scale * inv_loss_scale, d_sqnorm, d_overflow);
+    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, n > 0 ? nb : 0, inv2, d_scale,
+                       d_sqnorm, d_overflow, st_decide, h, grad_dtype == ZERO_F32 ? 1 : 0, coef);
     return launch_status("sqnorm_finalize");
+}
+
+int check_state(const zero_step_state* d_state) {
+    if (d_state == nullptr) return fail(ZERO_EINVAL, "d_state is NULL");
+    if ((uintptr_t)d_state & 7u) return fail(ZERO_EALIGN, "d_state must be 8-byte aligned");
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zero_shard
+
+extern "C" {
+
+int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
+                                     double* d_sqnorm, int32_t* d_overflow, void* d_workspace,
+                                     size_t workspace_bytes, void* hip_stream) {
+    clear_error();
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    return norm_pass(grad, grad_dtype, n, inv_loss_scale * inv_loss_scale, nullptr, d_sqnorm, d_overflow,
+                     d_workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream));
+}
+
+int zero_shard_unscale_norm_overflow_dev(const void* grad, int32_t grad_dtype, int64_t n,
+                                         const zero_step_state* d_state, double* d_sqnorm, int32_t* d_overflow,
+                                         void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+    clear_error();
+    const int st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    // an fp32 gradient is the accumulation or reduction copy, already unscaled
+    const double* d_scale = grad_dtype == ZERO_F32 ? nullptr : &d_state->scaler.scale;
+    return norm_pass(grad, grad_dtype, n, 1.0, d_scale, d_sqnorm, d_overflow, d_workspace, workspace_bytes,
+                     static_cast<hipStream_t>(hip_stream));
 }
 
 int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const void* grad, int32_t grad_dtype,
@@ -712,14 +809,72 @@ int zero_shard_adam_step_coef(float* master, float* exp_avg, float* exp_avg_sq, 
     return launch_status("adam_update_devcoef");
 }
 
-int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
-                               int32_t first, int32_t* d_overflow, void* hip_stream) {
+int zero_shard_norm_decide_dev(const void* grad, int32_t grad_dtype, int64_t n, const zero_adam_hyper* hp,
+                               zero_step_state* d_state, double* d_sqnorm, int32_t* d_overflow, void* d_coef,
+                               void* d_workspace, size_t workspace_bytes, void* hip_stream) {
     clear_error();
+    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
+    int st = check_hyper(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm);
+    if (st != ZERO_OK) return st;
+    st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    if (d_coef == nullptr || ((uintptr_t)d_coef & 7u)) return fail(ZERO_EINVAL, "d_coef NULL or not 8-byte aligned");
+    const HyperArgs h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm};
+    const double* d_scale = grad_dtype == ZERO_F32 ? nullptr : &d_state->scaler.scale;
+    return norm_pass(grad, grad_dtype, n, 1.0, d_scale, d_sqnorm, d_overflow, d_workspace, workspace_bytes,
+                     static_cast<hipStream_t>(hip_stream), d_state, h, static_cast<StepCoef*>(d_coef));
+}
+
+int zero_step_decide_dev(const zero_adam_hyper* hp, int32_t grad_dtype, zero_step_state* d_state,
+                         const int32_t* d_global_overflow, void* d_coef, void* hip_stream) {
+    clear_error();
+    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
+    int st = check_hyper(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm);
+    if (st != ZERO_OK) return st;
+    st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
+        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
+    if (d_global_overflow == nullptr || ((uintptr_t)d_global_overflow & 3u))
+        return fail(ZERO_EINVAL, "d_global_overflow NULL or misaligned");
+    if (d_coef == nullptr || ((uintptr_t)d_coef & 7u)) return fail(ZERO_EINVAL, "d_coef NULL or not 8-byte aligned");
+    const HyperArgs h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm};
+    hipLaunchKernelGGL(step_decide, dim3(1), dim3(64), 0, static_cast<hipStream_t>(hip_stream), d_state,
+                       d_global_overflow, h, grad_dtype == ZERO_F32 ? 1 : 0, static_cast<StepCoef*>(d_coef));
+    return launch_status("step_decide");
+}
+
+int zero_shard_adam_step_dev(float* master, float* exp_avg, float* exp_avg_sq, const void* grad, int32_t grad_dtype,
+                             void* param_out, int32_t param_dtype, int64_t n, const zero_adam_hyper* hp,
+                             zero_step_state* d_state, const double* d_global_sqnorm,
+                             const int32_t* d_global_overflow, void* d_coef, void* hip_stream) {
+    clear_error();
+    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
+    if (d_global_sqnorm == nullptr && hp->max_grad_norm > 0.0) return fail(ZERO_EINVAL, "clipping needs d_global_sqnorm");
+    // everything is checked before anything is enqueued
+    int st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n, d_global_sqnorm,
+                             d_global_overflow);
+    if (st != ZERO_OK) return st;
+    // the decision and the state update run even for an empty shard: every rank advances together
+    st = zero_step_decide_dev(hp, grad_dtype, d_state, d_global_overflow, d_coef, hip_stream);
+    if (st != ZERO_OK || n == 0) return st;
+    const StepCoef unused{};
+    launch_adam_any(grad_dtype, elementwise_grid(n, kAdamGroup), static_cast<hipStream_t>(hip_stream),
+                    param_out != nullptr, param_dtype, master, exp_avg, exp_avg_sq, grad, param_out, n, unused,
+                    static_cast<const StepCoef*>(d_coef), d_global_sqnorm, d_global_overflow);
+    return launch_status("adam_update_devcoef");
+}
+
+}  // extern "C"
+
+namespace zero_shard {
+namespace {
+
+int accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
+               const double* d_scale, int32_t first, int32_t* d_overflow, hipStream_t s) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
     if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16 (got %d)", grad_dtype);
-    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
-        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
     if (n == 0) return ZERO_OK;
     if (acc == nullptr || grad == nullptr) return fail(ZERO_EINVAL, "NULL acc or grad");
     if (!aligned16(acc) || !aligned16(grad)) return fail(ZERO_EALIGN, "acc and grad must be 16-byte aligned");
@@ -727,10 +882,9 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     if (overlaps(acc, n * 4, grad, n * 2)) return fail(ZERO_EINVAL, "acc aliases grad");
     const dim3 grid = elementwise_grid(n);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const float inv = (float)inv_loss_scale;
 #define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), 0, s, acc, grad, n, inv, \
-                                         d_overflow)
+                                         d_scale, d_overflow)
     if (grad_dtype == ZERO_F16) {
         if (first) ZS_ACC(ZERO_F16, true);
         else ZS_ACC(ZERO_F16, false);
@@ -742,16 +896,13 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
     return launch_status("grad_accumulate");
 }
 
-int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n,
-                           double inv_loss_scale, int32_t* d_overflow, void* hip_stream) {
-    clear_error();
+int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n,
+           double inv_loss_scale, const double* d_scale, int32_t* d_overflow, hipStream_t s) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
     if (n_slices < 1 || n_slices > ZERO_MAX_SLICES)
         return fail(ZERO_EINVAL, "n_slices must lie in [1, %d] (got %d)", ZERO_MAX_SLICES, n_slices);
     if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16)
         return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16 (got %d)", grad_dtype);
-    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
-        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
     if (n == 0) return ZERO_OK;
     if (acc == nullptr || slices == nullptr) return fail(ZERO_EINVAL, "NULL acc or slices");
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
@@ -765,15 +916,56 @@ int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slic
         sl.p[r] = slices[r];
     }
     const dim3 grid = elementwise_grid(n);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const float inv = (float)inv_loss_scale;
     if (grad_dtype == ZERO_F16)
         hipLaunchKernelGGL(grad_reduce<ZERO_F16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
-                           d_overflow);
+                           d_scale, d_overflow);
     else
         hipLaunchKernelGGL(grad_reduce<ZERO_BF16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
-                           d_overflow);
+                           d_scale, d_overflow);
     return launch_status("grad_reduce");
+}
+
+}  // namespace
+}  // namespace zero_shard
+
+extern "C" {
+
+int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
+                               int32_t first, int32_t* d_overflow, void* hip_stream) {
+    clear_error();
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    return accumulate(acc, grad, grad_dtype, n, inv_loss_scale, nullptr, first, d_overflow,
+                      static_cast<hipStream_t>(hip_stream));
+}
+
+int zero_shard_grad_accumulate_dev(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+                                   const zero_step_state* d_state, int32_t first, int32_t* d_overflow,
+                                   void* hip_stream) {
+    clear_error();
+    const int st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    return accumulate(acc, grad, grad_dtype, n, 1.0, &d_state->scaler.scale, first, d_overflow,
+                      static_cast<hipStream_t>(hip_stream));
+}
+
+int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n,
+                           double inv_loss_scale, int32_t* d_overflow, void* hip_stream) {
+    clear_error();
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    return reduce(acc, slices, n_slices, grad_dtype, n, inv_loss_scale, nullptr, d_overflow,
+                  static_cast<hipStream_t>(hip_stream));
+}
+
+int zero_shard_grad_reduce_dev(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                               int64_t n, const zero_step_state* d_state, int32_t* d_overflow, void* hip_stream) {
+    clear_error();
+    const int st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    return reduce(acc, slices, n_slices, grad_dtype, n, 1.0, &d_state->scaler.scale, d_overflow,
+                  static_cast<hipStream_t>(hip_stream));
 }
 
 // ---------------------------------------------------------------- step graphs

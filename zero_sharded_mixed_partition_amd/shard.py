@@ -8,20 +8,29 @@ pass, then read the 4-byte overflow flag back to update the loss scale and the
 step counter on the host.  The flag read is the step's only device-to-host
 transfer; the skip itself is decided on the device from the same flag, so the
 kernels never wait for the host.
+
+With device_state=True the loss scale and the step counter live in device
+memory instead (zero_step_state): the norm pass reads the scale there, and a
+one-thread kernel forms the step's coefficients and advances the scaler after
+the overflow flag is known.  A step then never waits for the device; step()
+returns None and read_state() brings the scaler and counts back on demand.
 """
 from typing import Callable, Optional
 
 import torch
 
-from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, dtype_code, zero_loss_scaler_update,
-               zero_norm_workspace_bytes, zero_shard_adam_step, zero_shard_grad_accumulate,
-               zero_shard_grad_reduce, zero_shard_unscale_norm_overflow)
+from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, StepState, dtype_code, zero_adam_coef_bytes,
+               zero_loss_scaler_update, zero_norm_workspace_bytes, zero_shard_adam_step,
+               zero_shard_grad_accumulate, zero_shard_grad_accumulate_dev, zero_shard_grad_reduce,
+               zero_shard_adam_step_coef, zero_shard_grad_reduce_dev, zero_shard_unscale_norm_overflow,
+               zero_shard_norm_decide_dev, zero_shard_unscale_norm_overflow_dev, zero_step_decide_dev)
 
 
 class ShardAdam:
     def __init__(self, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, *,
                  lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, max_grad_norm=0.0,
-                 scaler: Optional[LossScaler] = None, applied_steps: int = 0, graph: bool = False):
+                 scaler: Optional[LossScaler] = None, applied_steps: int = 0, graph: bool = False,
+                 device_state: bool = False):
         n = master.numel()
         for t in (master, exp_avg, exp_avg_sq):
             if t.dtype != torch.float32 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
@@ -42,6 +51,10 @@ class ShardAdam:
         self.graph = graph
         self._graph, self._graph_key = None, None
         self.recorded_this_step = False
+        if graph and device_state:
+            raise ValueError("graph=True records the host-scaled step; use one of graph and device_state")
+        self.state = StepState(self.scaler, applied_steps, dev) if device_state else None
+        self.d_coef = torch.empty(zero_adam_coef_bytes(), dtype=torch.uint8, device=dev) if device_state else None
 
     def _inv_scale(self, grad: torch.Tensor) -> float:
         # an fp32 gradient is the accumulation copy, already unscaled
@@ -51,29 +64,64 @@ class ShardAdam:
                    overflow: Optional[torch.Tensor] = None) -> None:
         """Enqueue one micro-batch into the fp32 gradient copy `acc`
         (acc = (first ? 0 : acc) + grad / loss_scale)."""
-        zero_shard_grad_accumulate(acc, grad, 1.0 / self.scaler.scale, first, overflow)
+        if self.state is not None:
+            zero_shard_grad_accumulate_dev(acc, grad, self.state, first, overflow)
+        else:
+            zero_shard_grad_accumulate(acc, grad, 1.0 / self.scaler.scale, first, overflow)
 
     def reduce(self, acc: torch.Tensor, slices, overflow: Optional[torch.Tensor] = None) -> None:
         """Enqueue the reduction of the data-parallel ranks' gradient slices of
         this partition into the fp32 gradient copy `acc` (slice order,
         acc = sum_k slice_k / loss_scale)."""
-        zero_shard_grad_reduce(acc, slices, 1.0 / self.scaler.scale, overflow)
+        if self.state is not None:
+            zero_shard_grad_reduce_dev(acc, slices, self.state, overflow)
+        else:
+            zero_shard_grad_reduce(acc, slices, 1.0 / self.scaler.scale, overflow)
 
     def unscale_norm(self, grad: torch.Tensor) -> None:
         """Enqueue steps 1-2: self.sqnorm, self.overflow <- this shard's values."""
+        if self.state is not None:
+            zero_shard_unscale_norm_overflow_dev(grad, self.state, self.sqnorm, self.overflow, self.workspace)
+            return
         zero_shard_unscale_norm_overflow(grad, self._inv_scale(grad), self.sqnorm, self.overflow, self.workspace)
 
     def apply(self, grad: torch.Tensor, param_out: Optional[torch.Tensor], global_sqnorm=None,
               global_overflow=None) -> None:
         """Enqueue steps 3-4 for step index t+1 (skipped on device on overflow)."""
+        if self.state is not None:
+            self.decide(grad, global_overflow)
+            self.update(grad, param_out, global_sqnorm, global_overflow)
+            return
         hp = AdamHyper(step=self.t + 1, inv_loss_scale=self._inv_scale(grad), **self.hyper)
         zero_shard_adam_step(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out, hp,
                              self.sqnorm if global_sqnorm is None else global_sqnorm,
                              self.overflow if global_overflow is None else global_overflow,
                              grad_dtype=dtype_code(grad))
 
+    def norm_decide(self, grad: torch.Tensor) -> None:
+        """device_state, one rank: the norm pass with the decision folded
+        into its final kernel."""
+        zero_shard_norm_decide_dev(grad, AdamHyper(**self.hyper), self.state, self.sqnorm, self.overflow,
+                                   self.d_coef, self.workspace)
+
+    def decide(self, grad: torch.Tensor, global_overflow=None) -> None:
+        """device_state: enqueue the decision kernel (coefficients of the
+        next step into d_coef, scaler and counts advanced by the flag)."""
+        zero_step_decide_dev(AdamHyper(**self.hyper), grad.dtype, self.state,
+                             self.overflow if global_overflow is None else global_overflow, self.d_coef)
+
+    def update(self, grad: torch.Tensor, param_out: Optional[torch.Tensor], global_sqnorm=None,
+               global_overflow=None) -> None:
+        """device_state: enqueue the fused update with the coefficients in d_coef."""
+        zero_shard_adam_step_coef(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out, self.d_coef,
+                                  self.sqnorm if global_sqnorm is None else global_sqnorm,
+                                  self.overflow if global_overflow is None else global_overflow)
+
     def finish(self, global_overflow: Optional[torch.Tensor] = None) -> bool:
-        """Read the overflow flag, update the loss scale and t; returns skip."""
+        """Read the overflow flag, update the loss scale and t; returns skip
+        (None with device_state: nothing to do on the host)."""
+        if self.state is not None:
+            return None
         flag = self.overflow if global_overflow is None else global_overflow
         self._flag_host.copy_(flag, non_blocking=True)
         self._flag_ready.record()
@@ -88,14 +136,26 @@ class ShardAdam:
         """One full step.  `allreduce(sqnorm, overflow)`, if given, must turn
         this rank's two scalars into the data-parallel sum / OR in place (on
         one GPU the shard's own values are the global ones).  Returns True if
-        the step was skipped."""
+        the step was skipped (None with device_state, which never waits)."""
         if self.graph and allreduce is None:
             return self._graph_step(grad, param_out)
+        if self.state is not None and allreduce is None:
+            self.norm_decide(grad)          # one rank: its flag is the global one
+            self.update(grad, param_out)
+            return None
         self.unscale_norm(grad)
         if allreduce is not None:
             allreduce(self.sqnorm, self.overflow)
         self.apply(grad, param_out)
         return self.finish()
+
+    def read_state(self):
+        """device_state: copy the state to the host (waits for the steps
+        enqueued so far), refresh self.t and self.scaler from it and return it."""
+        st = self.state.read()
+        self.t = st.applied
+        self.scaler.s = type(self.scaler.s).from_buffer_copy(bytes(st.scaler))
+        return st
 
     def _graph_step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor]) -> bool:
         inv = self._inv_scale(grad)
