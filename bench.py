@@ -227,15 +227,15 @@ def main():
     ap.add_argument("--offload", action="store_true",
                     help="keep the fp32 state in pinned host memory and step on host cores (CPU offload)")
     ap.add_argument("--graph", action="store_true",
-                    help="replay one recorded step graph per step (norm pass, fused update and flag read as a "
-                         "single launch; pays off on small shards where launches dominate)")
+                    help="replay one recorded step graph per step (the step's kernels as a single launch; pays off "
+                         "on small shards where launches dominate)")
     ap.add_argument("--host-scaler", action="store_true",
                     help="keep the loss scaler and step counter on the host, reading the 4-byte overflow flag back "
                          "every step (default: both live in device memory and no step waits for the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.graph and (args.accum or args.offload or args.reduce):
-        print("--graph records the host-scaled 16-bit-gradient step on the GPU; it does not combine with --accum, "
+        print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum, "
               "--reduce or --offload", file=sys.stderr)
         sys.exit(2)
     if args.reduce and (args.accum or args.offload or not 1 <= args.reduce <= 16):
@@ -276,7 +276,7 @@ def main():
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
                       applied_steps=w.step - 1, graph=args.graph,
-                      device_state=not (args.host_scaler or args.graph))
+                      device_state=not args.host_scaler)
     DS = opt.state is not None
     K = args.accum
     R = args.reduce
@@ -332,7 +332,13 @@ def main():
     t0 = time.perf_counter()
     for k in range(args.steps):
         ts = time.perf_counter()
-        skipped += bool(step(None if args.graph else evs[k]))  # host scaler: ends with the flag read
+        if args.graph:
+            evs[k][6].record()
+            r = step(None)
+            evs[k][2].record()
+        else:
+            r = step(evs[k])
+        skipped += bool(r)                                     # host scaler: the step ended with the flag read
         wall.append(time.perf_counter() - ts)
     torch.cuda.synchronize()
     t1 = time.perf_counter()

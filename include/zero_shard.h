@@ -400,6 +400,23 @@ int zero_shard_grad_accumulate_dev(float* acc, const void* grad, int32_t grad_dt
 int zero_shard_grad_reduce_dev(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
                                int64_t n, const zero_step_state* d_state, int32_t* d_overflow, void* hip_stream);
 
+/* A recorded step with device state: zero_shard_norm_decide_dev then
+ * zero_shard_adam_step_coef on these buffers, captured once as a HIP graph
+ * (kernels only: no host blocks, no copies).  Each launch replays one whole
+ * step of one rank; the loss scale, t and the skip come from d_state, so
+ * nothing changes between replays and no launch waits.  The hyperparameters
+ * are recorded with the graph (record a new one when they change).
+ * create ALLOCATES (the graph and an event); destroy frees them and waits for
+ * the last replay.  zero_step_graph_launch / _overflow reject such a graph,
+ * and zero_step_graph_launch_dev rejects the host-coefficient kind.
+ * Errors: as zero_shard_norm_decide_dev and zero_shard_adam_step_coef, plus
+ * ZERO_EHIP from capture or launch. */
+int zero_step_graph_create_dev(zero_step_graph** out, float* master, float* exp_avg, float* exp_avg_sq,
+                               const void* grad, int32_t grad_dtype, void* param_out, int32_t param_dtype,
+                               int64_t n, const zero_adam_hyper* hp, zero_step_state* d_state, double* d_sqnorm,
+                               int32_t* d_overflow, void* d_coef, void* d_workspace, size_t workspace_bytes);
+int zero_step_graph_launch_dev(zero_step_graph* g, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * Measurement aid (not a step of the method): a plain device copy, one
  * 16-byte vector per lane, in the same streaming style as the step's kernels.

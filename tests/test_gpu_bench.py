@@ -11,7 +11,8 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.parametrize("extra", [[], ["--graph", "--no-cpu-baseline"], ["--reduce", "3", "--no-cpu-baseline"],
+@pytest.mark.parametrize("extra", [[], ["--graph", "--no-cpu-baseline"], ["--graph", "--host-scaler", "--no-cpu-baseline"],
+                                   ["--reduce", "3", "--no-cpu-baseline"],
                                    ["--host-scaler", "--accum", "2", "--no-cpu-baseline"]])
 def test_bench_json_line(extra):
     torch = pytest.importorskip("torch")

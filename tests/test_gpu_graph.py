@@ -111,3 +111,47 @@ def test_coef_entry_point_matches_by_value(Z):
                      V.cpu().numpy().view(np.uint32), bits_of(par)])
     for a, b in zip(*outs):
         assert (a == b).all()
+
+
+@pytest.mark.parametrize("wname,n", [("tiny", 196_864), ("gpt100b", 500_003)])
+def test_device_state_graph_replays_match_eager(Z, wname, n):
+    """The recorded device-state step (kernels only) against the eager
+    device-state step: 8 steps with an overflow, back-off and growth, torch
+    work and synchronisations between replays, a gradient-buffer change (one
+    re-recording); every replay bit-identical, scaler and counts equal."""
+    w = W.get(wname)
+    p, m, v, _ = W.shard_inputs(w, 0, n)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    hyper = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                 max_grad_norm=w.max_grad_norm)
+    mk = lambda g: Z.ShardAdam(to_device(p), to_device(m), to_device(v), applied_steps=w.step - 1,  # noqa: E731
+                               scaler=Z.LossScaler(scale=w.loss_scale, growth_interval=3), device_state=True,
+                               graph=g, **hyper)
+    eager, graph = mk(False), mk(True)
+    par_e = torch.zeros(n, dtype=tdt[w.param_dtype], device="cuda")
+    par_g = torch.zeros(n, dtype=tdt[w.param_dtype], device="cuda")
+    grads = [torch.empty(n, dtype=tdt[w.grad_dtype], device="cuda") for _ in range(2)]
+    side = torch.randn(1 << 20, device="cuda")
+    recorded = []
+    for it in range(1, 9):
+        scale = eager.read_state().scaler.scale
+        g = W.fill(w, "grad", 0, n, step=40 + it, loss_scale=scale)
+        if it == 3:
+            g[n // 4] = W.POS_INF_BITS[w.grad_dtype]
+        G = grads[0 if it < 6 else 1]
+        G.copy_(to_device(g, w.grad_dtype))
+        eager.step(G, par_e)
+        side.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        graph.step(G, par_g)
+        side.abs_().sqrt_()
+        recorded.append(graph.recorded_this_step)
+        se, sg = eager.read_state(), graph.read_state()
+        assert bytes(se) == bytes(sg), f"iteration {it}"
+        assert sg.last_overflow == (it == 3)
+        for a, b in ((eager.master, graph.master), (eager.exp_avg, graph.exp_avg),
+                     (eager.exp_avg_sq, graph.exp_avg_sq)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"iteration {it}"
+        assert torch.equal(par_e.view(torch.int16), par_g.view(torch.int16))
+    assert recorded == [True, False, False, False, False, True, False, False]
+    assert sg.skipped == 1 and sg.applied == w.step - 1 + 7

@@ -33,7 +33,7 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
            "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
-           "zero_shard_norm_decide_dev"]
+           "zero_shard_norm_decide_dev", "StepGraphDev"]
 
 
 def zero_abi_version() -> int:
@@ -407,6 +407,42 @@ def zero_shard_grad_reduce_dev(acc, slices, state: StepState, overflow=None, gra
     arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
     _L.check(_L.lib().zero_shard_grad_reduce_dev(_ptr(acc), arr, len(slices), gd, n, state.ptr(), _ptr(overflow),
                                                  _stream(stream)), "zero_shard_grad_reduce_dev")
+
+
+class StepGraphDev:
+    """A recorded step with device state (zero_step_graph_create_dev): the
+    norm pass with the decision, then the update, replayed by launch() with
+    no host work besides the launch.  The library allocates the graph;
+    close() (or garbage collection) frees it."""
+
+    def __init__(self, master, exp_avg, exp_avg_sq, grad, param_out, hp: "AdamHyper", state: StepState, sqnorm,
+                 overflow, d_coef, workspace, grad_dtype: Optional[int] = None, param_dtype: Optional[int] = None):
+        gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+        pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
+        handle = ctypes.c_void_p()
+        h = _hyper(hp)
+        _L.check(_L.lib().zero_step_graph_create_dev(ctypes.byref(handle), _ptr(master), _ptr(exp_avg),
+                                                     _ptr(exp_avg_sq), _ptr(grad), gd, _ptr(param_out), pd,
+                                                     master.numel(), ctypes.byref(h), state.ptr(), _ptr(sqnorm),
+                                                     _ptr(overflow), _ptr(d_coef), _ptr(workspace),
+                                                     workspace.numel() * workspace.element_size()),
+                 "zero_step_graph_create_dev")
+        self._h = handle.value
+        self._keep = (master, exp_avg, exp_avg_sq, grad, param_out, state, sqnorm, overflow, d_coef, workspace)
+
+    def launch(self, stream=None) -> None:
+        _L.check(_L.lib().zero_step_graph_launch_dev(self._h, _stream(stream)), "zero_step_graph_launch_dev")
+
+    def close(self) -> None:
+        if self._h:
+            _L.lib().zero_step_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class LossScaler:

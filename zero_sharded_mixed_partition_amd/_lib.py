@@ -63,6 +63,9 @@ SIGNATURES = {
     "zero_step_graph_launch": (c_i32, [c_vp, ctypes.POINTER(zero_adam_params), c_vp]),
     "zero_step_graph_overflow": (c_i32, [c_vp, P_i32]),
     "zero_step_graph_destroy": (c_i32, [c_vp]),
+    "zero_step_graph_create_dev": (c_i32, [ctypes.POINTER(c_vp), c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
+                                           ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz]),
+    "zero_step_graph_launch_dev": (c_i32, [c_vp, c_vp]),
     "zero_cpu_shard_unscale_norm_overflow": (c_i32, [c_vp, c_i32, c_i64, c_dbl, ctypes.POINTER(c_dbl), P_i32, c_i32]),
     "zero_cpu_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),

@@ -979,6 +979,7 @@ struct zero_step_graph {
     StepCoef* d_coef = nullptr;      // device copy read by the update kernel
     double inv_loss_scale = 1.0;
     bool launched = false;
+    bool device_state = false;       // recorded by zero_step_graph_create_dev: no host blocks
 };
 
 static void release_graph(zero_step_graph* g) {
@@ -1052,6 +1053,7 @@ int zero_step_graph_create(zero_step_graph** out, float* master, float* exp_avg,
 int zero_step_graph_launch(zero_step_graph* g, const zero_adam_params* hp, void* hip_stream) {
     clear_error();
     if (g == nullptr) return fail(ZERO_EINVAL, "graph is NULL");
+    if (g->device_state) return fail(ZERO_EINVAL, "graph recorded with device state: use zero_step_graph_launch_dev");
     StepCoef c;
     const int pst = prepare_adam(hp, &c);
     if (pst != ZERO_OK) return pst;
@@ -1074,6 +1076,7 @@ int zero_step_graph_launch(zero_step_graph* g, const zero_adam_params* hp, void*
 int zero_step_graph_overflow(zero_step_graph* g, int32_t* overflow) {
     clear_error();
     if (g == nullptr || overflow == nullptr) return fail(ZERO_EINVAL, "NULL argument");
+    if (g->device_state) return fail(ZERO_EINVAL, "graph recorded with device state: read the state instead");
     if (!g->launched) return fail(ZERO_EINVAL, "graph not launched yet");
     const hipError_t e = hipEventSynchronize(g->done);
     if (e != hipSuccess) return fail(ZERO_EHIP, "waiting for the replay: %s", hipGetErrorString(e));
@@ -1081,10 +1084,74 @@ int zero_step_graph_overflow(zero_step_graph* g, int32_t* overflow) {
     return ZERO_OK;
 }
 
+int zero_step_graph_create_dev(zero_step_graph** out, float* master, float* exp_avg, float* exp_avg_sq,
+                               const void* grad, int32_t grad_dtype, void* param_out, int32_t param_dtype, int64_t n,
+                               const zero_adam_hyper* hp, zero_step_state* d_state, double* d_sqnorm,
+                               int32_t* d_overflow, void* d_coef, void* d_workspace, size_t workspace_bytes) {
+    clear_error();
+    if (out == nullptr) return fail(ZERO_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (hp == nullptr) return fail(ZERO_EINVAL, "hp is NULL");
+    int st = check_hyper(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm);
+    if (st != ZERO_OK) return st;
+    st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    if (d_coef == nullptr || ((uintptr_t)d_coef & 7u)) return fail(ZERO_EINVAL, "d_coef NULL or not 8-byte aligned");
+    if (d_sqnorm == nullptr || d_overflow == nullptr || d_workspace == nullptr)
+        return fail(ZERO_EINVAL, "NULL norm output or workspace");
+    if (((uintptr_t)d_sqnorm & 7u) || ((uintptr_t)d_overflow & 3u) || !aligned16(d_workspace))
+        return fail(ZERO_EALIGN, "norm outputs or workspace misaligned");
+    if (workspace_bytes < zero_norm_workspace_bytes(n)) return fail(ZERO_ENOSPC, "workspace too small");
+    st = check_step_args(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n, d_sqnorm,
+                         d_overflow);
+    if (st != ZERO_OK) return st;
+    zero_step_graph* g = new zero_step_graph();
+    g->device_state = true;
+    hipStream_t cs = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&g->done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreate(&cs);
+    if (e != hipSuccess) {
+        if (cs) (void)hipStreamDestroy(cs);
+        release_graph(g);
+        return fail(ZERO_EHIP, "step graph resources: %s", hipGetErrorString(e));
+    }
+    // record: the norm pass with the decision in its last kernel, then the update
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        st = zero_shard_norm_decide_dev(grad, grad_dtype, n, hp, d_state, d_sqnorm, d_overflow, d_coef, d_workspace,
+                                        workspace_bytes, cs);
+        if (st == ZERO_OK)
+            st = zero_shard_adam_step_coef(master, exp_avg, exp_avg_sq, grad, grad_dtype, param_out, param_dtype, n,
+                                           d_coef, d_sqnorm, d_overflow, cs);
+        e = hipStreamEndCapture(cs, &g->graph);
+    }
+    if (e == hipSuccess && st == ZERO_OK) e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    (void)hipStreamDestroy(cs);
+    if (e != hipSuccess || st != ZERO_OK) {
+        release_graph(g);
+        if (st != ZERO_OK) return st;
+        return fail(ZERO_EHIP, "step graph capture: %s", hipGetErrorString(e));
+    }
+    *out = g;
+    return ZERO_OK;
+}
+
+int zero_step_graph_launch_dev(zero_step_graph* g, void* hip_stream) {
+    clear_error();
+    if (g == nullptr) return fail(ZERO_EINVAL, "graph is NULL");
+    if (!g->device_state) return fail(ZERO_EINVAL, "graph recorded with host coefficients: use zero_step_graph_launch");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipGraphLaunch(g->exec, s);
+    if (e == hipSuccess) e = hipEventRecord(g->done, s);      // lets destroy wait for the last replay
+    if (e != hipSuccess) return fail(ZERO_EHIP, "graph launch: %s", hipGetErrorString(e));
+    g->launched = true;
+    return ZERO_OK;
+}
+
 int zero_step_graph_destroy(zero_step_graph* g) {
     clear_error();
     if (g == nullptr) return ZERO_OK;
-    if (g->launched) (void)hipEventSynchronize(g->done);
+    if (g->launched && g->done != nullptr) (void)hipEventSynchronize(g->done);
     release_graph(g);
     return ZERO_OK;
 }

@@ -19,7 +19,7 @@ from typing import Callable, Optional
 
 import torch
 
-from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, StepState, dtype_code, zero_adam_coef_bytes,
+from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, StepGraphDev, StepState, dtype_code, zero_adam_coef_bytes,
                zero_loss_scaler_update, zero_norm_workspace_bytes, zero_shard_adam_step,
                zero_shard_grad_accumulate, zero_shard_grad_accumulate_dev, zero_shard_grad_reduce,
                zero_shard_adam_step_coef, zero_shard_grad_reduce_dev, zero_shard_unscale_norm_overflow,
@@ -51,8 +51,6 @@ class ShardAdam:
         self.graph = graph
         self._graph, self._graph_key = None, None
         self.recorded_this_step = False
-        if graph and device_state:
-            raise ValueError("graph=True records the host-scaled step; use one of graph and device_state")
         self.state = StepState(self.scaler, applied_steps, dev) if device_state else None
         self.d_coef = torch.empty(zero_adam_coef_bytes(), dtype=torch.uint8, device=dev) if device_state else None
 
@@ -138,6 +136,9 @@ class ShardAdam:
         one GPU the shard's own values are the global ones).  Returns True if
         the step was skipped (None with device_state, which never waits)."""
         if self.graph and allreduce is None:
+            if self.state is not None:
+                self._graph_step_dev(grad, param_out)
+                return None
             return self._graph_step(grad, param_out)
         if self.state is not None and allreduce is None:
             self.norm_decide(grad)          # one rank: its flag is the global one
@@ -156,6 +157,20 @@ class ShardAdam:
         self.t = st.applied
         self.scaler.s = type(self.scaler.s).from_buffer_copy(bytes(st.scaler))
         return st
+
+    def _graph_step_dev(self, grad: torch.Tensor, param_out: Optional[torch.Tensor]) -> None:
+        # with device state a recording depends only on the buffers (and the hyperparameters)
+        key = ("dev", grad.data_ptr(), grad.dtype, grad.numel(),
+               None if param_out is None else (param_out.data_ptr(), param_out.dtype), tuple(self.hyper.items()))
+        self.recorded_this_step = key != self._graph_key
+        if self.recorded_this_step:
+            if self._graph is not None:
+                self._graph.close()
+            self._graph = StepGraphDev(self.master, self.exp_avg, self.exp_avg_sq, grad, param_out,
+                                       AdamHyper(**self.hyper), self.state, self.sqnorm, self.overflow, self.d_coef,
+                                       self.workspace)
+            self._graph_key = key
+        self._graph.launch()
 
     def _graph_step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor]) -> bool:
         inv = self._inv_scale(grad)
