@@ -340,3 +340,65 @@ def test_decode_agrees_with_library_on_workload_grads():
     w = W.GPT2_SMALL
     g = W.fill(w, "grad", 0, 4096, step=w.step)
     assert (decode16(g, "f16") == _lib_vals(g, "f16")).all()
+
+
+# ---------------------------------------------------------------- scalar brute force
+
+def _f32(x: float) -> float:
+    """Round a Python float to IEEE binary32 (round to nearest even) with struct."""
+    import struct
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _half_bits(x: float) -> int:
+    """IEEE binary16 bits of x, round to nearest even (struct's 'e' format)."""
+    import struct
+    return struct.unpack("<H", struct.pack("<e", x))[0]
+
+
+def _decode_half(b: int) -> float:
+    import struct
+    return struct.unpack("<e", struct.pack("<H", b))[0]
+
+
+def _scalar_step(p, m, v, gbits, inv, max_norm, lr, b1, b2, eps, wd, t):
+    """The whole step element by element in plain Python floats (IEEE double),
+    written from the textbook definitions with no vector code: unscale,
+    exact sum of squares (math.fsum), clip coefficient, AdamW with bias
+    correction, float32 storage, fp16 writeback."""
+    g = [_decode_half(b) * inv for b in gbits]
+    norm = math.sqrt(math.fsum(x * x for x in g))
+    coef = min(1.0, max_norm / (norm + 1e-6)) if max_norm > 0 else 1.0
+    out = []
+    for pi, mi, vi, gi in zip(p, m, v, g):
+        gi = gi * coef
+        mi2 = b1 * mi + (1 - b1) * gi
+        vi2 = b2 * vi + (1 - b2) * gi * gi
+        mhat = mi2 / (1 - b1 ** t)
+        vhat = vi2 / (1 - b2 ** t)
+        pi2 = pi - lr * (mhat / (math.sqrt(vhat) + eps) + wd * pi)
+        p32 = _f32(pi2)
+        out.append((p32, _f32(mi2), _f32(vi2), _half_bits(p32)))
+    return out
+
+
+@pytest.mark.parametrize("n,t,max_norm", [(1, 1, 0.0), (7, 3, 1.0), (64, 100, 0.05), (64, 1, 1e9)])
+def test_scalar_loop_equals_vectorised(n, t, max_norm):
+    """Brute force on tiny shards: a per-element pure-Python step equals the
+    vectorised oracle (state to 1 float32 ulp, parameters bit for bit)."""
+    rng = np.random.default_rng(n * 31 + t)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = rng.uniform(1e-8, 1e-5, n).astype(np.float32)
+    gbits = _rand_bits(rng, n, "f16", 1e-3 * 1024)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    inv = 2.0**-10
+    sq, ovf = shard_sqnorm_overflow(gbits, "f16", inv)
+    got = shard_step(p, m, v, gbits, "f16", "f16", global_sq=sq, global_overflow=ovf, inv_loss_scale=inv,
+                     max_grad_norm=max_norm, step=t, **hp)
+    ref = _scalar_step(p.tolist(), m.tolist(), v.tolist(), gbits.tolist(), inv, max_norm, hp["lr"], hp["beta1"],
+                       hp["beta2"], hp["eps"], hp["weight_decay"], t)
+    for k, name in enumerate(("master", "exp_avg", "exp_avg_sq")):
+        r = np.array([e[k] for e in ref], np.float32)
+        assert (np.abs(got[k].astype(np.float64) - r.astype(np.float64)) <= np.abs(np.spacing(r))).all(), name
+    assert [int(b) for b in got[3]] == [e[3] for e in ref]

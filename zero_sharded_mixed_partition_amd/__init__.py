@@ -475,3 +475,4 @@ def zero_loss_scaler_update(scaler: LossScaler, overflow: bool) -> bool:
 
 from .shard import ShardAdam  # noqa: E402
 from .offload import OffloadShardAdam  # noqa: E402
+from . import checkpoint  # noqa: E402,F401

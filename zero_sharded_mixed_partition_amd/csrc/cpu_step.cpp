@@ -36,7 +36,22 @@ namespace {
 constexpr int64_t kChunk = int64_t(1) << 16;   // elements per work item / norm partial
 constexpr int kTile = 2048;                    // elements converted per inner pass (stack buffers)
 
+// Per-ISA clones of the hot loops (AVX-512, AVX2, baseline), picked at load
+// time by resolvers the dynamic loader runs.  A ThreadSanitizer build compiles
+// them once: its runtime is not up yet when the loader runs the resolvers.
+#if defined(__has_feature)
+#if __has_feature(thread_sanitizer)
+#define ZS_SINGLE_ISA 1
+#endif
+#endif
+#if defined(__SANITIZE_THREAD__)
+#define ZS_SINGLE_ISA 1
+#endif
+#ifdef ZS_SINGLE_ISA
+#define ZS_CLONES
+#else
 #define ZS_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#endif
 
 inline uint32_t f2u(float f) {
     uint32_t u;
