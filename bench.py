@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--reduce", type=int, default=0,
                     help="K: the step's gradient is the reduction of K ranks' 16-bit slices of this partition "
                          "into the fp32 copy (the local half of the gradient reduce-scatter)")
+    ap.add_argument("--separate-norm", action="store_true",
+                    help="with --accum/--reduce: run the norm pass over the fp32 copy on its own instead of in the "
+                         "pass that writes the copy")
     ap.add_argument("--offload", action="store_true",
                     help="keep the fp32 state in pinned host memory and step on host cores (CPU offload)")
     ap.add_argument("--graph", action="store_true",
@@ -278,6 +281,7 @@ def main():
                       applied_steps=w.step - 1, graph=args.graph,
                       device_state=not args.host_scaler)
     DS = opt.state is not None
+    FUSED = bool(args.accum or args.reduce) and not args.separate_norm
     K = args.accum
     R = args.reduce
     A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
@@ -294,24 +298,29 @@ def main():
             for k in range(K):
                 if ev is not None and k == K - 1:
                     ev[3].record()
-                opt.accumulate(A, G, first=(k == 0))
+                opt.accumulate(A, G, first=(k == 0), last=FUSED and k == K - 1)
             if ev is not None:
                 ev[4].record()
         if R:
             if ev is not None:
                 ev[3].record()
-            opt.reduce(A, slices)
+            opt.reduce(A, slices, with_norm=FUSED)
             if ev is not None:
                 ev[4].record()
         grad = A if (K or R) else G
         if ev is not None:
             ev[0].record()
-        if DS:
+        if FUSED:
+            pass                               # the copy's norm and flag came with the pass that wrote it
+        elif DS:
             opt.norm_decide(grad)              # the decision (coefficients, scaler, counts) in the norm's last kernel
         else:
             opt.unscale_norm(grad)
         if ev is not None:
             ev[1].record()
+        if FUSED and DS:
+            opt.decide(grad)                   # one thread: coefficients, scaler, counts
+        if ev is not None:
             ev[5].record()
         if DS:
             opt.update(grad, par)
@@ -385,26 +394,29 @@ def main():
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
     adam_bpp = ADAM_F32_BYTES_PER_PARAM if (K or R) else ADAM_BYTES_PER_PARAM
-    norm_bpp = NORM_F32_BYTES_PER_PARAM if (K or R) else NORM_BYTES_PER_PARAM
+    norm_bpp = 0 if FUSED else (NORM_F32_BYTES_PER_PARAM if (K or R) else NORM_BYTES_PER_PARAM)
     acc_bpp = (ACC_FIRST_BYTES_PER_PARAM + ACC_BYTES_PER_PARAM * (K - 1)) if K else 0
     red_bpp = 2 * R + 4 if R else 0
     step_bpp = adam_bpp + norm_bpp + acc_bpp + red_bpp
     adam_avg = mean(adam_ms)
     adam_gbps = adam_bpp * S / (adam_avg * 1e-3) / 1e9
     step_gbps = step_bpp * S / (ms_step * 1e-3) / 1e9
-    run_key = w.name + (f"+accum{K}" if K else "") + (f"+reduce{R}" if R else "") + ("+graph" if args.graph else "")
+    run_key = w.name + (f"+accum{K}" if K else "") + (f"+reduce{R}" if R else "") + ("+graph" if args.graph else "") \
+        + ("+separate-norm" if (K or R) and not FUSED else "")
     traffic = measured_traffic(run_key)
     accum_stats = None
     if K:
         acc_ms = mean([e[3].elapsed_time(e[4]) for e in evs])     # the last (non-first) accumulation
-        accum_stats = {"micro_batches": K, "kernel": "grad_accumulate", "avg_ms": acc_ms,
+        accum_stats = {"micro_batches": K, "kernel": "grad_sum_norm (with the norm)" if FUSED else "grad_accumulate",
+                       "avg_ms": acc_ms,
                        "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
                        "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
                        "traffic": measured_traffic(run_key, "grad_accumulate")}
     reduce_stats = None
     if R:
         red_ms = mean([e[3].elapsed_time(e[4]) for e in evs])
-        reduce_stats = {"slices": R, "kernel": "grad_reduce", "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
+        reduce_stats = {"slices": R, "kernel": "grad_sum_norm (with the norm)" if FUSED else "grad_reduce",
+                        "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
                         "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9, "traffic": measured_traffic(run_key, "grad_reduce")}
 
     # the achievable rate of one read + one write stream over the same 14 B/param
@@ -449,6 +461,7 @@ def main():
                    "weight_decay": w.weight_decay, "param_layout": w.param_layout,
                    "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else
                             f"reduction of {R} ranks' 16-bit slices into the fp32 copy" if R else "16-bit gradient")
+                   + ((", norm in the pass that writes the copy" if FUSED else ", separate norm pass") if (K or R) else "")
                    + (", recorded step graph" if args.graph else "")
                    + (", scaler and step counter in device memory" if DS else ", host loss scaler (4-byte flag read per step)"),
                    "algorithmic_bytes_per_param": step_bpp},
@@ -461,7 +474,8 @@ def main():
                      "timed_on": "eager launches after the timed region" if args.graph else "the timed steps"},
         "step_ms": {"median": pct(sorted(wall), 0.5) * 1e3, "p10": pct(sorted(wall), 0.1) * 1e3,
                     "p90": pct(sorted(wall), 0.9) * 1e3},
-        "norm_pass": {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9},
+        "norm_pass": ({"fused_into": "grad_sum_norm"} if FUSED else
+                      {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9}),
         "skipped_step": {"steps": n_skip, "ms_per_step": mean(skip_wall) * 1e3,
                          "norm_ms": mean([e[0].elapsed_time(e[1]) for e in sev]),
                          "update_ms": mean([e[5].elapsed_time(e[2]) for e in sev])},

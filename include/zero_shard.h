@@ -418,6 +418,43 @@ int zero_step_graph_create_dev(zero_step_graph** out, float* master, float* exp_
 int zero_step_graph_launch_dev(zero_step_graph* g, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * The fp32 gradient copy and its norm in one pass (fp32 accumulation and the
+ * local half of the reduce-scatter above, fused with the norm pass).
+ *
+ * zero_shard_grad_sum_norm writes
+ *     acc = (add_to_acc ? acc : 0) + sum_k slices[k] * inv_loss_scale,
+ * slice by slice with one fp32 rounding per addition (bit-identical to
+ * zero_shard_grad_reduce, or to zero_shard_grad_accumulate for one slice),
+ * and in the same pass the squared L2 norm and the inf/NaN flag of the
+ * result: *d_sqnorm = sum acc^2 (the copy is already unscaled), *d_overflow
+ * = 1 if any element of acc is inf or NaN (it then equals +inf or NaN, as
+ * the norm pass reports).  This replaces the norm pass over the copy (4
+ * bytes per element).  Use it for the reduction of K ranks' slices
+ * (add_to_acc = 0) or for the last micro-batch of an accumulation
+ * (add_to_acc = 1 after the first, one slice).
+ * The norm is summed in fp64, per one-wave task of 256 elements, then over
+ * tasks and blocks in a fixed order: deterministic, but summed in another
+ * order than the norm pass, so its last bits may differ from it.
+ *  d_workspace  device scratch of zero_sum_norm_workspace_bytes(n) bytes,
+ *               16-byte aligned (about n/32 bytes), not overlapping acc
+ * zero_shard_grad_sum_norm_dev: the same with inv_loss_scale = 1/scale
+ *   read from d_state; with hp given (one rank, whose flag is the global
+ *   one) its final kernel also makes the step's decision into d_coef, as
+ *   zero_shard_norm_decide_dev does; with hp NULL the caller runs
+ *   zero_step_decide_dev after the data-parallel reduction.
+ * Streams 2K + 4 bytes per element (2K + 8 with add_to_acc).
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_ENOSPC, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+size_t zero_sum_norm_workspace_bytes(int64_t n);
+int zero_shard_grad_sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                             int64_t n, int32_t add_to_acc, double inv_loss_scale, double* d_sqnorm,
+                             int32_t* d_overflow, void* d_workspace, size_t workspace_bytes, void* hip_stream);
+int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                                 int64_t n, int32_t add_to_acc, const zero_adam_hyper* hp,
+                                 zero_step_state* d_state, double* d_sqnorm, int32_t* d_overflow, void* d_coef,
+                                 void* d_workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement aid (not a step of the method): a plain device copy, one
  * 16-byte vector per lane, in the same streaming style as the step's kernels.
  * Its rate is the achievable rate of one read plus one write stream, which

@@ -343,3 +343,29 @@ def test_norm_decide_rejects_bad_arguments_on_host():
     assert nd(al, L.ZERO_F16, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, None, al + 384, 1024, None) == L.ZERO_EINVAL
     assert nd(al, 7, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, al + 320, al + 384, 1024, None) == L.ZERO_EINVAL
     assert nd(al, L.ZERO_F16, 8, ctypes.byref(hp), al + 512, al + 256, al + 264, al + 320, al + 384, 0, None) == L.ZERO_ENOSPC
+
+
+def test_sum_norm_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(2048)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    f = lib.zero_shard_grad_sum_norm
+    one = (ctypes.c_void_p * 1)(al + 256)
+    ws = Z.zero_sum_norm_workspace_bytes(8)
+    assert f(al, one, 0, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 768, ws, None) == L.ZERO_EINVAL
+    assert f(al, one, 1, L.ZERO_F32, 8, 0, 1.0, al + 512, al + 520, al + 768, ws, None) == L.ZERO_EINVAL
+    assert f(al, one, 1, L.ZERO_F16, 8, 0, 0.0, al + 512, al + 520, al + 768, ws, None) == L.ZERO_EINVAL
+    assert f(al, one, 1, L.ZERO_F16, 8, 0, 1.0, None, al + 520, al + 768, ws, None) == L.ZERO_EINVAL
+    assert f(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 768, 0, None) == L.ZERO_ENOSPC
+    assert f(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 776, ws, None) == L.ZERO_EALIGN
+    assert f(al, (ctypes.c_void_p * 1)(al + 8), 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 768, ws,
+             None) == L.ZERO_EALIGN
+    assert f(al, (ctypes.c_void_p * 1)(al + 16), 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 768, ws,
+             None) == L.ZERO_EINVAL                                      # acc aliases the slice
+    g = lib.zero_shard_grad_sum_norm_dev
+    hp = L.zero_adam_hyper(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0)
+    assert g(al, one, 1, L.ZERO_F16, 8, 0, None, None, al + 512, al + 520, None, al + 768, ws, None) == L.ZERO_EINVAL
+    assert g(al, one, 1, L.ZERO_F16, 8, 0, ctypes.byref(hp), al + 1024, al + 512, al + 520, None, al + 768, ws,
+             None) == L.ZERO_EINVAL                                      # decision without d_coef
+    assert Z.zero_sum_norm_workspace_bytes(-1) == 0
+    assert Z.zero_sum_norm_workspace_bytes(976077312) < 976077312 // 16

@@ -17,7 +17,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-STREAMING = ("adam_update", "adam_update_devcoef", "grad_accumulate", "grad_reduce", "sqnorm_partials")
+STREAMING = ("adam_update", "adam_update_devcoef", "grad_accumulate", "grad_reduce", "grad_sum_norm",
+             "sqnorm_partials")
 
 
 @pytest.fixture(scope="module")

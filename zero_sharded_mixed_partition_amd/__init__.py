@@ -33,7 +33,8 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
            "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
-           "zero_shard_norm_decide_dev", "StepGraphDev"]
+           "zero_shard_norm_decide_dev", "StepGraphDev", "zero_sum_norm_workspace_bytes", "zero_shard_grad_sum_norm",
+           "zero_shard_grad_sum_norm_dev"]
 
 
 def zero_abi_version() -> int:
@@ -407,6 +408,42 @@ def zero_shard_grad_reduce_dev(acc, slices, state: StepState, overflow=None, gra
     arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
     _L.check(_L.lib().zero_shard_grad_reduce_dev(_ptr(acc), arr, len(slices), gd, n, state.ptr(), _ptr(overflow),
                                                  _stream(stream)), "zero_shard_grad_reduce_dev")
+
+
+def zero_sum_norm_workspace_bytes(n: int) -> int:
+    return int(_L.lib().zero_sum_norm_workspace_bytes(int(n)))
+
+
+def zero_shard_grad_sum_norm(acc, slices, add_to_acc: bool, inv_loss_scale: float, sqnorm, overflow, workspace,
+                             grad_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
+    """acc = (add_to_acc ? acc : 0) + sum_k slices[k] * inv, with the norm and
+    flag of the result in the same pass (sqnorm, overflow: device scalars)."""
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
+    gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
+    _L.check(_L.lib().zero_shard_grad_sum_norm(_ptr(acc), arr, len(slices), gd, n, 1 if add_to_acc else 0,
+                                               float(inv_loss_scale), _ptr(sqnorm), _ptr(overflow), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)),
+             "zero_shard_grad_sum_norm")
+
+
+def zero_shard_grad_sum_norm_dev(acc, slices, add_to_acc: bool, state: StepState, sqnorm, overflow, workspace,
+                                 hp: Optional["AdamHyper"] = None, d_coef=None, grad_dtype: Optional[int] = None,
+                                 n: Optional[int] = None, stream=None) -> None:
+    """zero_shard_grad_sum_norm with the loss scale from the device state; with
+    hp (one rank) the final kernel also makes the step's decision into d_coef."""
+    if not 1 <= len(slices) <= MAX_SLICES:
+        raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
+    gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
+    n = acc.numel() if n is None else n
+    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
+    h = None if hp is None else ctypes.byref(_hyper(hp))
+    _L.check(_L.lib().zero_shard_grad_sum_norm_dev(_ptr(acc), arr, len(slices), gd, n, 1 if add_to_acc else 0, h,
+                                                   state.ptr(), _ptr(sqnorm), _ptr(overflow), _ptr(d_coef),
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(stream)), "zero_shard_grad_sum_norm_dev")
 
 
 class StepGraphDev:

@@ -66,6 +66,12 @@ SIGNATURES = {
     "zero_step_graph_create_dev": (c_i32, [ctypes.POINTER(c_vp), c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                            ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz]),
     "zero_step_graph_launch_dev": (c_i32, [c_vp, c_vp]),
+    "zero_sum_norm_workspace_bytes": (c_sz, [c_i64]),
+    "zero_shard_grad_sum_norm": (c_i32, [c_vp, ctypes.POINTER(c_vp), c_i32, c_i32, c_i64, c_i32, c_dbl, c_vp, c_vp,
+                                         c_vp, c_sz, c_vp]),
+    "zero_shard_grad_sum_norm_dev": (c_i32, [c_vp, ctypes.POINTER(c_vp), c_i32, c_i32, c_i64, c_i32,
+                                             ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                             c_vp]),
     "zero_cpu_shard_unscale_norm_overflow": (c_i32, [c_vp, c_i32, c_i64, c_dbl, ctypes.POINTER(c_dbl), P_i32, c_i32]),
     "zero_cpu_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),

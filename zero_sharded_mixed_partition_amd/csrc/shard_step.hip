@@ -591,6 +591,89 @@ __global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A,
     if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
 }
 
+// ---------------------------------------------------------------- fp32 copy with its norm in the same pass
+
+// acc = (ADD ? acc : 0) + sum_k slice_k * inv in slice order (the same
+// operations as grad_accumulate / grad_reduce), and, per one-wave task, the
+// fp64 sum of the squares of the 256 results it wrote: one partial per task
+// in part_task, summed over the wave in a fixed xor-butterfly order.  A
+// non-finite result makes its partial non-finite (the square of a finite
+// fp32 value, and any sum of up to 2^40 of them, stays finite in fp64), so
+// the overflow flag is read off the partials.
+template <int DT, bool ADD>
+__global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ A, SlicePtrs sl, int k, int64_t n,
+                                                            float inv, const double* __restrict__ d_scale,
+                                                            double* __restrict__ part_task) {
+    if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
+    const int lane = threadIdx.x;
+    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
+    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
+        double sq = 0.0;
+        const int64_t e0 = t * kEwTask + 4 * lane;
+        if (e0 + 4 <= n) {
+            const int64_t q = e0 >> 2;
+            u32x2 w[ZERO_MAX_SLICES];
+#pragma unroll
+            for (int r = 0; r < ZERO_MAX_SLICES; ++r)
+                if (r < k) w[r] = ld_stream(static_cast<const u32x2*>(sl.p[r]) + q);
+            f32x4 a;
+            if constexpr (ADD) a = ld_stream(reinterpret_cast<const f32x4*>(A) + q);
+#pragma unroll
+            for (int r = 0; r < ZERO_MAX_SLICES; ++r) {
+                if (r < k) {
+                    float g[4];
+                    unpack2<DT>(w[r][0], g[0], g[1]);
+                    unpack2<DT>(w[r][1], g[2], g[3]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[j] = (!ADD && r == 0) ? g[j] * inv : fmaf(g[j], inv, a[j]);
+                }
+            }
+            st_stream(a, reinterpret_cast<f32x4*>(A) + q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double x = (double)a[j];
+                sq = fma(x, x, sq);
+            }
+        } else if (e0 < n) {
+            for (int64_t e = e0; e < n; ++e) {
+                float a = ADD ? A[e] : 0.0f;
+                for (int r = 0; r < k; ++r) {
+                    const float g = load_grad1<DT>(sl.p[r], e);
+                    a = (!ADD && r == 0) ? g * inv : fmaf(g, inv, a);
+                }
+                A[e] = a;
+                const double x = (double)a;
+                sq = fma(x, x, sq);
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 64);
+        if (lane == 0) st_stream(sq, part_task + t);        // read once, by task_partials_reduce
+    }
+}
+
+// The task partials into at most kNormMaxBlocks block partials: block b sums
+// its contiguous range of tasks in a fixed order; bad = any non-finite partial.
+__global__ __launch_bounds__(kBlock) void task_partials_reduce(const double* __restrict__ part_task, int64_t ntasks,
+                                                               int64_t per_block, double* __restrict__ part_sq,
+                                                               uint32_t* __restrict__ part_bad) {
+    __shared__ double s_sq[kWaves];
+    __shared__ uint32_t s_bad[kWaves];
+    const int64_t lo = (int64_t)blockIdx.x * per_block;
+    const int64_t hi = lo + per_block < ntasks ? lo + per_block : ntasks;
+    double acc = 0.0;
+    uint32_t bad = 0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+        const double x = part_task[i];
+        bad |= ((__double_as_longlong(x) >> 52) & 0x7FF) == 0x7FF ? 1u : 0u;
+        acc += x;
+    }
+    block_reduce(acc, bad, s_sq, s_bad);
+    if (threadIdx.x == 0) {
+        part_sq[blockIdx.x] = acc;
+        part_bad[blockIdx.x] = bad;
+    }
+}
+
 // ---------------------------------------------------------------- host helpers
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -926,6 +1009,86 @@ int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad
     return launch_status("grad_reduce");
 }
 
+// Layout of the fused pass's workspace: one double per task, then the block
+// partials of the norm pass (double, uint32).
+struct SumNormLayout {
+    int64_t ntasks;
+    int nb;
+    int64_t per_block;
+    size_t bytes;
+};
+
+SumNormLayout sum_norm_layout(int64_t n) {
+    SumNormLayout l;
+    l.ntasks = (n + kEwTask - 1) / kEwTask;
+    int64_t nb = l.ntasks / 1024;
+    if (nb < 1) nb = 1;
+    if (nb > kNormMaxBlocks) nb = kNormMaxBlocks;
+    l.nb = (int)nb;
+    l.per_block = (l.ntasks + nb - 1) / nb;
+    const size_t raw = (size_t)(l.ntasks + nb) * sizeof(double) + (size_t)nb * sizeof(uint32_t);
+    l.bytes = (raw + 255) & ~(size_t)255;
+    return l;
+}
+
+int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n, int32_t add,
+             double inv_loss_scale, const double* d_scale, double* d_sqnorm, int32_t* d_overflow, void* d_workspace,
+             size_t workspace_bytes, hipStream_t s, zero_step_state* st_decide, const HyperArgs& h, StepCoef* coef) {
+    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
+    if (n_slices < 1 || n_slices > ZERO_MAX_SLICES)
+        return fail(ZERO_EINVAL, "n_slices must lie in [1, %d] (got %d)", ZERO_MAX_SLICES, n_slices);
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16)
+        return fail(ZERO_EINVAL, "grad_dtype must be ZERO_F16 or ZERO_BF16 (got %d)", grad_dtype);
+    if (d_sqnorm == nullptr || d_overflow == nullptr || d_workspace == nullptr)
+        return fail(ZERO_EINVAL, "NULL norm output or workspace");
+    if (((uintptr_t)d_sqnorm & 7u) || ((uintptr_t)d_overflow & 3u) || !aligned16(d_workspace))
+        return fail(ZERO_EALIGN, "norm outputs or workspace misaligned");
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    const SumNormLayout l = sum_norm_layout(n);
+    if (workspace_bytes < l.bytes) return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, l.bytes);
+    SlicePtrs sl{};
+    if (n > 0) {
+        if (acc == nullptr || slices == nullptr) return fail(ZERO_EINVAL, "NULL acc or slices");
+        if (!aligned16(acc)) return fail(ZERO_EALIGN, "acc must be 16-byte aligned");
+        if (overlaps(acc, n * 4, d_workspace, (int64_t)workspace_bytes)) return fail(ZERO_EINVAL, "acc aliases workspace");
+        for (int32_t r = 0; r < n_slices; ++r) {
+            if (slices[r] == nullptr) return fail(ZERO_EINVAL, "slice %d is NULL", r);
+            if (!aligned16(slices[r])) return fail(ZERO_EALIGN, "slice %d must be 16-byte aligned", r);
+            if (overlaps(acc, n * 4, slices[r], n * 2)) return fail(ZERO_EINVAL, "acc aliases slice %d", r);
+            sl.p[r] = slices[r];
+        }
+    }
+    double* part_task = static_cast<double*>(d_workspace);
+    double* part_sq = part_task + l.ntasks;
+    uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + l.nb);
+    int nparts = 0;
+    if (n > 0) {
+        const dim3 grid = elementwise_grid(n);
+        const float inv = (float)inv_loss_scale;
+#define ZS_SUM(DT, ADD) hipLaunchKernelGGL((grad_sum_norm<DT, ADD>), grid, dim3(kEwThreads), 0, s, acc, sl, \
+                                           (int)n_slices, n, inv, d_scale, part_task)
+        if (grad_dtype == ZERO_F16) {
+            if (add) ZS_SUM(ZERO_F16, true);
+            else ZS_SUM(ZERO_F16, false);
+        } else {
+            if (add) ZS_SUM(ZERO_BF16, true);
+            else ZS_SUM(ZERO_BF16, false);
+        }
+#undef ZS_SUM
+        int st = launch_status("grad_sum_norm");
+        if (st != ZERO_OK) return st;
+        hipLaunchKernelGGL(task_partials_reduce, dim3(l.nb), dim3(kBlock), 0, s, part_task, l.ntasks, l.per_block,
+                           part_sq, part_bad);
+        st = launch_status("task_partials_reduce");
+        if (st != ZERO_OK) return st;
+        nparts = l.nb;
+    }
+    // the copy is already unscaled: the factor on the sum of squares is 1
+    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, nparts, 1.0, nullptr, d_sqnorm,
+                       d_overflow, st_decide, h, 1, coef);
+    return launch_status("sqnorm_finalize");
+}
+
 }  // namespace
 }  // namespace zero_shard
 
@@ -966,6 +1129,41 @@ int zero_shard_grad_reduce_dev(float* acc, const void* const* slices, int32_t n_
     if (st != ZERO_OK) return st;
     return reduce(acc, slices, n_slices, grad_dtype, n, 1.0, &d_state->scaler.scale, d_overflow,
                   static_cast<hipStream_t>(hip_stream));
+}
+
+size_t zero_sum_norm_workspace_bytes(int64_t n) {
+    if (n < 0) return 0;
+    return sum_norm_layout(n).bytes;
+}
+
+int zero_shard_grad_sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n,
+                             int32_t add_to_acc, double inv_loss_scale, double* d_sqnorm, int32_t* d_overflow,
+                             void* d_workspace, size_t workspace_bytes, void* hip_stream) {
+    clear_error();
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    return sum_norm(acc, slices, n_slices, grad_dtype, n, add_to_acc, inv_loss_scale, nullptr, d_sqnorm, d_overflow,
+                    d_workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream), nullptr, HyperArgs{}, nullptr);
+}
+
+int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype,
+                                 int64_t n, int32_t add_to_acc, const zero_adam_hyper* hp, zero_step_state* d_state,
+                                 double* d_sqnorm, int32_t* d_overflow, void* d_coef, void* d_workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+    clear_error();
+    int st = check_state(d_state);
+    if (st != ZERO_OK) return st;
+    HyperArgs h{};
+    if (hp != nullptr) {
+        st = check_hyper(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm);
+        if (st != ZERO_OK) return st;
+        if (d_coef == nullptr || ((uintptr_t)d_coef & 7u))
+            return fail(ZERO_EINVAL, "d_coef NULL or not 8-byte aligned");
+        h = HyperArgs{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm};
+    }
+    return sum_norm(acc, slices, n_slices, grad_dtype, n, add_to_acc, 1.0, &d_state->scaler.scale, d_sqnorm,
+                    d_overflow, d_workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream),
+                    hp != nullptr ? d_state : nullptr, h, static_cast<StepCoef*>(d_coef));
 }
 
 // ---------------------------------------------------------------- step graphs

@@ -22,7 +22,8 @@ import torch
 from . import (ZERO_F32, AdamHyper, LossScaler, StepGraph, StepGraphDev, StepState, dtype_code, zero_adam_coef_bytes,
                zero_loss_scaler_update, zero_norm_workspace_bytes, zero_shard_adam_step,
                zero_shard_grad_accumulate, zero_shard_grad_accumulate_dev, zero_shard_grad_reduce,
-               zero_shard_adam_step_coef, zero_shard_grad_reduce_dev, zero_shard_unscale_norm_overflow,
+               zero_shard_adam_step_coef, zero_shard_grad_reduce_dev, zero_shard_grad_sum_norm,
+               zero_shard_grad_sum_norm_dev, zero_sum_norm_workspace_bytes, zero_shard_unscale_norm_overflow,
                zero_shard_norm_decide_dev, zero_shard_unscale_norm_overflow_dev, zero_step_decide_dev)
 
 
@@ -52,25 +53,45 @@ class ShardAdam:
         self._graph, self._graph_key = None, None
         self.recorded_this_step = False
         self.state = StepState(self.scaler, applied_steps, dev) if device_state else None
+        self._sum_ws = None           # workspace of the fused copy-and-norm pass, made on first use
         self.d_coef = torch.empty(zero_adam_coef_bytes(), dtype=torch.uint8, device=dev) if device_state else None
 
     def _inv_scale(self, grad: torch.Tensor) -> float:
         # an fp32 gradient is the accumulation copy, already unscaled
         return 1.0 if dtype_code(grad) == ZERO_F32 else 1.0 / self.scaler.scale
 
+    def _sum_norm(self, acc: torch.Tensor, slices, add: bool) -> None:
+        if self._sum_ws is None:
+            self._sum_ws = torch.empty(zero_sum_norm_workspace_bytes(self.n), dtype=torch.uint8, device=acc.device)
+        if self.state is not None:
+            zero_shard_grad_sum_norm_dev(acc, slices, add, self.state, self.sqnorm, self.overflow, self._sum_ws)
+        else:
+            zero_shard_grad_sum_norm(acc, slices, add, 1.0 / self.scaler.scale, self.sqnorm, self.overflow,
+                                     self._sum_ws)
+
     def accumulate(self, acc: torch.Tensor, grad: torch.Tensor, first: bool,
-                   overflow: Optional[torch.Tensor] = None) -> None:
+                   overflow: Optional[torch.Tensor] = None, last: bool = False) -> None:
         """Enqueue one micro-batch into the fp32 gradient copy `acc`
-        (acc = (first ? 0 : acc) + grad / loss_scale)."""
+        (acc = (first ? 0 : acc) + grad / loss_scale).  last=True fuses the
+        norm pass of the finished copy into this pass; then call
+        step(acc, ..., norm_done=True)."""
+        if last:
+            self._sum_norm(acc, [grad], not first)
+            return
         if self.state is not None:
             zero_shard_grad_accumulate_dev(acc, grad, self.state, first, overflow)
         else:
             zero_shard_grad_accumulate(acc, grad, 1.0 / self.scaler.scale, first, overflow)
 
-    def reduce(self, acc: torch.Tensor, slices, overflow: Optional[torch.Tensor] = None) -> None:
+    def reduce(self, acc: torch.Tensor, slices, overflow: Optional[torch.Tensor] = None,
+               with_norm: bool = False) -> None:
         """Enqueue the reduction of the data-parallel ranks' gradient slices of
         this partition into the fp32 gradient copy `acc` (slice order,
-        acc = sum_k slice_k / loss_scale)."""
+        acc = sum_k slice_k / loss_scale).  with_norm=True fuses the norm pass
+        of the copy into it; then call step(acc, ..., norm_done=True)."""
+        if with_norm:
+            self._sum_norm(acc, slices, False)
+            return
         if self.state is not None:
             zero_shard_grad_reduce_dev(acc, slices, self.state, overflow)
         else:
@@ -130,11 +151,23 @@ class ShardAdam:
         return skip
 
     def step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor] = None,
-             allreduce: Optional[Callable[[torch.Tensor, torch.Tensor], None]] = None) -> bool:
+             allreduce: Optional[Callable[[torch.Tensor, torch.Tensor], None]] = None,
+             norm_done: bool = False) -> bool:
         """One full step.  `allreduce(sqnorm, overflow)`, if given, must turn
         this rank's two scalars into the data-parallel sum / OR in place (on
         one GPU the shard's own values are the global ones).  Returns True if
-        the step was skipped (None with device_state, which never waits)."""
+        the step was skipped (None with device_state, which never waits).
+        norm_done: the norm and flag of `grad` (the fp32 copy) were formed by
+        accumulate(last=True) or reduce(with_norm=True)."""
+        if norm_done:
+            if allreduce is not None:
+                allreduce(self.sqnorm, self.overflow)
+            if self.state is not None:
+                self.decide(grad)
+                self.update(grad, param_out)
+                return None
+            self.apply(grad, param_out)
+            return self.finish()
         if self.graph and allreduce is None:
             if self.state is not None:
                 self._graph_step_dev(grad, param_out)
