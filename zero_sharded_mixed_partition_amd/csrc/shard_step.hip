@@ -540,12 +540,14 @@ __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict_
 // The K ranks' 16-bit gradients of this partition, summed in slice order into
 // fp32 with one rounding per addition; the same operations, in the same
 // order, as K passes of grad_accumulate (first on slice 0).
-struct SlicePtrs {
-    const void* p[ZERO_MAX_SLICES];
+// Slice pointers passed by value; MAXK is the capacity compiled in.
+template <int MAXK>
+struct SlicesOf {
+    const void* p[MAXK];
 };
 
-template <int DT>
-__global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A, SlicePtrs sl, int k, int64_t n,
+template <int DT, int MAXK>
+__global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A, SlicesOf<MAXK> sl, int k, int64_t n,
                                                           float inv, const double* __restrict__ d_scale,
                                                           int32_t* __restrict__ d_ovf) {
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
@@ -556,14 +558,14 @@ __global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A,
         const int64_t e0 = t * kEwTask + 4 * lane;
         if (e0 + 4 <= n) {
             const int64_t q = e0 >> 2;
-            u32x2 w[ZERO_MAX_SLICES];
+            u32x2 w[MAXK];
             // every slice's load in flight before any math (k is uniform)
 #pragma unroll
-            for (int r = 0; r < ZERO_MAX_SLICES; ++r)
+            for (int r = 0; r < MAXK; ++r)
                 if (r < k) w[r] = ld_stream(static_cast<const u32x2*>(sl.p[r]) + q);
             f32x4 a;
 #pragma unroll
-            for (int r = 0; r < ZERO_MAX_SLICES; ++r) {
+            for (int r = 0; r < MAXK; ++r) {
                 if (r < k) {
                     bad |= (w[r][0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
                     bad |= (w[r][1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
@@ -591,17 +593,48 @@ __global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A,
     if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
 }
 
+// ---------------------------------------------------------------- wave sum through DPP
+
+// v + (v moved by the DPP control CTRL within the rows in ROW_MASK; lanes with
+// no source, or outside ROW_MASK, add 0), on both 32-bit halves of a double.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add(double v) {
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    const int mlo = __builtin_amdgcn_update_dpp(0, lo, CTRL, ROW_MASK, 0xF, true);
+    const int mhi = __builtin_amdgcn_update_dpp(0, hi, CTRL, ROW_MASK, 0xF, true);
+    return v + __hiloint2double(mhi, mlo);
+}
+
+// Sum over the 64 lanes of a wave (all lanes active), in a fixed order, with
+// VALU data movement only: shifts right by 1, 2, 4, 8 within each 16-lane row
+// leave the row sums in lanes 15, 31, 47, 63; lane 15's row sum is broadcast
+// into row 1 and lane 47's into row 3, then lane 31 into rows 2 and 3, so
+// lane 63 holds the total, which every lane reads back.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+__device__ __forceinline__ double wave_sum(double v) {
+    v = dpp_add<kDppRowShr1, 0xF>(v);
+    v = dpp_add<kDppRowShr2, 0xF>(v);
+    v = dpp_add<kDppRowShr4, 0xF>(v);
+    v = dpp_add<kDppRowShr8, 0xF>(v);
+    v = dpp_add<kDppRowBcast15, 0xA>(v);
+    v = dpp_add<kDppRowBcast31, 0xC>(v);
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+    return __hiloint2double(hi, lo);
+}
+
 // ---------------------------------------------------------------- fp32 copy with its norm in the same pass
 
 // acc = (ADD ? acc : 0) + sum_k slice_k * inv in slice order (the same
 // operations as grad_accumulate / grad_reduce), and, per one-wave task, the
 // fp64 sum of the squares of the 256 results it wrote: one partial per task
-// in part_task, summed over the wave in a fixed xor-butterfly order.  A
+// in part_task, summed over the wave in a fixed order (wave_sum).  A
 // non-finite result makes its partial non-finite (the square of a finite
 // fp32 value, and any sum of up to 2^40 of them, stays finite in fp64), so
 // the overflow flag is read off the partials.
-template <int DT, bool ADD>
-__global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ A, SlicePtrs sl, int k, int64_t n,
+template <int DT, bool ADD, int MAXK>
+__global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ A, SlicesOf<MAXK> sl, int k, int64_t n,
                                                             float inv, const double* __restrict__ d_scale,
                                                             double* __restrict__ part_task) {
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
@@ -612,14 +645,14 @@ __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ 
         const int64_t e0 = t * kEwTask + 4 * lane;
         if (e0 + 4 <= n) {
             const int64_t q = e0 >> 2;
-            u32x2 w[ZERO_MAX_SLICES];
+            u32x2 w[MAXK];
 #pragma unroll
-            for (int r = 0; r < ZERO_MAX_SLICES; ++r)
+            for (int r = 0; r < MAXK; ++r)
                 if (r < k) w[r] = ld_stream(static_cast<const u32x2*>(sl.p[r]) + q);
             f32x4 a;
             if constexpr (ADD) a = ld_stream(reinterpret_cast<const f32x4*>(A) + q);
 #pragma unroll
-            for (int r = 0; r < ZERO_MAX_SLICES; ++r) {
+            for (int r = 0; r < MAXK; ++r) {
                 if (r < k) {
                     float g[4];
                     unpack2<DT>(w[r][0], g[0], g[1]);
@@ -646,7 +679,7 @@ __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ 
                 sq = fma(x, x, sq);
             }
         }
-        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 64);
+        sq = wave_sum(sq);
         if (lane == 0) st_stream(sq, part_task + t);        // read once, by task_partials_reduce
     }
 }
@@ -953,6 +986,43 @@ int zero_shard_adam_step_dev(float* master, float* exp_avg, float* exp_avg_sq, c
 namespace zero_shard {
 namespace {
 
+// The slice-taking kernels are compiled for slice capacities 1, 2, 4, 8 and 16
+// and launched with the smallest one that holds n_slices: each pointer held
+// costs two scalar registers, and at capacity 16 their count limits
+// occupancy to 7 waves per SIMD (8 below).
+template <int MAXK>
+SlicesOf<MAXK> first_slices(const SlicesOf<ZERO_MAX_SLICES>& sl) {
+    SlicesOf<MAXK> r{};
+    for (int i = 0; i < MAXK; ++i) r.p[i] = sl.p[i];
+    return r;
+}
+
+template <int DT, bool ADD>
+void launch_sum_norm(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
+                     float inv, const double* d_scale, double* part_task) {
+#define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), 0, s, acc, \
+                                     first_slices<M>(sl), (int)k, n, inv, d_scale, part_task)
+    if (k <= 1) ZS_SUM(1);
+    else if (k <= 2) ZS_SUM(2);
+    else if (k <= 4) ZS_SUM(4);
+    else if (k <= 8) ZS_SUM(8);
+    else ZS_SUM(16);
+#undef ZS_SUM
+}
+
+template <int DT>
+void launch_reduce(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
+                   float inv, const double* d_scale, int32_t* d_overflow) {
+#define ZS_RED(M) hipLaunchKernelGGL((grad_reduce<DT, M>), grid, dim3(kEwThreads), 0, s, acc, first_slices<M>(sl), \
+                                     (int)k, n, inv, d_scale, d_overflow)
+    if (k <= 1) ZS_RED(1);
+    else if (k <= 2) ZS_RED(2);
+    else if (k <= 4) ZS_RED(4);
+    else if (k <= 8) ZS_RED(8);
+    else ZS_RED(16);
+#undef ZS_RED
+}
+
 int accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, double inv_loss_scale,
                const double* d_scale, int32_t first, int32_t* d_overflow, hipStream_t s) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
@@ -991,7 +1061,7 @@ int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     if (!aligned16(acc)) return fail(ZERO_EALIGN, "acc must be 16-byte aligned");
     if (d_overflow && ((uintptr_t)d_overflow & 3u)) return fail(ZERO_EALIGN, "d_overflow misaligned");
-    SlicePtrs sl{};
+    SlicesOf<ZERO_MAX_SLICES> sl{};
     for (int32_t r = 0; r < n_slices; ++r) {
         if (slices[r] == nullptr) return fail(ZERO_EINVAL, "slice %d is NULL", r);
         if (!aligned16(slices[r])) return fail(ZERO_EALIGN, "slice %d must be 16-byte aligned", r);
@@ -1000,12 +1070,8 @@ int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad
     }
     const dim3 grid = elementwise_grid(n);
     const float inv = (float)inv_loss_scale;
-    if (grad_dtype == ZERO_F16)
-        hipLaunchKernelGGL(grad_reduce<ZERO_F16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
-                           d_scale, d_overflow);
-    else
-        hipLaunchKernelGGL(grad_reduce<ZERO_BF16>, grid, dim3(kEwThreads), 0, s, acc, sl, (int)n_slices, n, inv,
-                           d_scale, d_overflow);
+    if (grad_dtype == ZERO_F16) launch_reduce<ZERO_F16>(grid, s, acc, sl, n_slices, n, inv, d_scale, d_overflow);
+    else launch_reduce<ZERO_BF16>(grid, s, acc, sl, n_slices, n, inv, d_scale, d_overflow);
     return launch_status("grad_reduce");
 }
 
@@ -1046,7 +1112,7 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     const SumNormLayout l = sum_norm_layout(n);
     if (workspace_bytes < l.bytes) return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, l.bytes);
-    SlicePtrs sl{};
+    SlicesOf<ZERO_MAX_SLICES> sl{};
     if (n > 0) {
         if (acc == nullptr || slices == nullptr) return fail(ZERO_EINVAL, "NULL acc or slices");
         if (!aligned16(acc)) return fail(ZERO_EALIGN, "acc must be 16-byte aligned");
@@ -1065,16 +1131,13 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
     if (n > 0) {
         const dim3 grid = elementwise_grid(n);
         const float inv = (float)inv_loss_scale;
-#define ZS_SUM(DT, ADD) hipLaunchKernelGGL((grad_sum_norm<DT, ADD>), grid, dim3(kEwThreads), 0, s, acc, sl, \
-                                           (int)n_slices, n, inv, d_scale, part_task)
         if (grad_dtype == ZERO_F16) {
-            if (add) ZS_SUM(ZERO_F16, true);
-            else ZS_SUM(ZERO_F16, false);
+            if (add) launch_sum_norm<ZERO_F16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
+            else launch_sum_norm<ZERO_F16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
         } else {
-            if (add) ZS_SUM(ZERO_BF16, true);
-            else ZS_SUM(ZERO_BF16, false);
+            if (add) launch_sum_norm<ZERO_BF16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
+            else launch_sum_norm<ZERO_BF16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
         }
-#undef ZS_SUM
         int st = launch_status("grad_sum_norm");
         if (st != ZERO_OK) return st;
         hipLaunchKernelGGL(task_partials_reduce, dim3(l.nb), dim3(kBlock), 0, s, part_task, l.ntasks, l.per_block,
