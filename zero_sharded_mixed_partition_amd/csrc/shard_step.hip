@@ -22,15 +22,30 @@
 //          exact fp64 squares per thread in a fixed order, reduces within a
 //          wave by xor-shuffles and across the block's four waves through
 //          LDS, then a one-block kernel combines the block partials in a
-//          fixed order.  Only the first block touches the ragged remainder.
+//          fixed order (and multiplies by 1/scale^2).  Only the first block
+//          touches the ragged remainder.
 //  adam_update: 28 B/element (2 grad + 4 master + 4 m + 4 v read, 4 + 4 + 4
 //          written back, 2 param written; 30 with an fp32 gradient).  One
 //          wave64 per workgroup, lane l owning 4 consecutive elements, so
 //          each access instruction is one contiguous, fully used run of
 //          cache lines; the number of resident waves per CU is capped.
+//          adam_update_devcoef is the same body with its coefficients read
+//          from device memory.
 //  grad_accumulate: acc = (first ? 0 : acc) + g * inv_scale into the fp32
 //          gradient copy, 10 B/element (6 for the first micro-batch), the
 //          same lane layout as adam_update but with no occupancy cap.
+//  grad_reduce: acc = sum over K ranks' 16-bit slices * inv_scale, in slice
+//          order (the local half of the gradient reduce-scatter), 2K + 4 B.
+//  grad_sum_norm + task_partials_reduce: the accumulation or the reduction
+//          with the norm of the result formed in the same pass (one fp64
+//          partial per one-wave task, folded in a fixed order), so the
+//          norm pass over the fp32 copy is not needed.
+//  step_decide (and sqnorm_finalize's decision): with the loss scaler and
+//          step counter in device memory, one thread forms the step's
+//          coefficient block and advances the scaler from the overflow flag.
+// The host-side entry points at the end check every argument before
+// enqueuing anything, and the step-graph calls record these passes as HIP
+// graphs.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
