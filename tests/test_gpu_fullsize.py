@@ -67,14 +67,6 @@ def _upload(w, begin, S, idx, step):
     return (P, M, V, G), {k: np.concatenate(a) for k, a in host.items()}, ref_sq, ref_ovf
 
 
-def _norm(Z, G, inv):
-    sq = torch.empty(1, dtype=torch.float64, device="cuda")
-    ovf = torch.empty(1, dtype=torch.int32, device="cuda")
-    ws = torch.empty(Z.zero_norm_workspace_bytes(G.numel()), dtype=torch.uint8, device="cuda")
-    Z.zero_shard_unscale_norm_overflow(G, inv, sq, ovf, ws)
-    return sq, ovf
-
-
 @pytest.mark.parametrize("wname", ["gpt1t", "llama7b"])
 def test_single_step_full_shard(Z, wname):
     w = W.get(wname)
@@ -85,14 +77,18 @@ def test_single_step_full_shard(Z, wname):
     (P, M, V, G), h, ref_sq, ref_ovf = _upload(w, begin, S, idx, w.step)
     par = torch.empty(S, dtype=TDT[w.param_dtype], device="cuda")
     inv = 1.0 / w.loss_scale
-    sq, ovf = _norm(Z, G, inv)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               max_grad_norm=w.max_grad_norm, step=w.step, inv_loss_scale=inv)
-    # one rank's shard: its own sum of squares stands in for the all-reduced one
-    Z.zero_shard_adam_step(P, M, V, G, par, Z.AdamHyper(**hp), sq, ovf)
-    torch.cuda.synchronize()
-    assert int(ovf.item()) == int(ref_ovf) == 0
-    check_norm(sq.item(), ref_sq)
+    # the launch configuration bench.py times: step state in device memory, the
+    # decision in the norm pass's last kernel, the update reading the device
+    # coefficients; one rank's own sum of squares stands in for the all-reduced one
+    opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                      max_grad_norm=w.max_grad_norm, applied_steps=w.step - 1, device_state=True,
+                      scaler=Z.LossScaler.static(w.loss_scale))
+    opt.step(G, par)
+    st = opt.read_state()
+    assert st.last_overflow == int(ref_ovf) == 0 and st.applied == w.step
+    check_norm(opt.sqnorm.item(), ref_sq)
     idx_t = torch.from_numpy(idx).cuda()
     got = (_gather(P, idx_t).cpu().numpy(), _gather(M, idx_t).cpu().numpy(), _gather(V, idx_t).cpu().numpy(),
            bits_of(_gather(par, idx_t)))
@@ -107,11 +103,13 @@ def test_single_step_full_shard(Z, wname):
     torch.cuda.empty_cache()
 
 
-def test_trajectory_with_overflow_full_shard(Z):
+@pytest.mark.parametrize("device_state", [True, False])
+def test_trajectory_with_overflow_full_shard(Z, device_state):
     """One rank's 250M-parameter shard of a 100B model over 20 steps with
     +inf injected into 0.1% of the gradient at iterations 5 and 12: skip
     decisions, loss scale and step counter bit-exact; norms and sampled
-    state within tolerance after every applied step."""
+    state within tolerance after every applied step (step state in device
+    memory, as bench.py runs it, and on the host)."""
     w = W.GPT_100B_RANK
     _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
     begin = w.rank * S
@@ -132,15 +130,18 @@ def test_trajectory_with_overflow_full_shard(Z):
     ref_m = np.zeros_like(ref_p)
     ref_v = np.zeros_like(ref_p)
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                      max_grad_norm=w.max_grad_norm, scaler=Z.LossScaler(scale=w.loss_scale))
+                      max_grad_norm=w.max_grad_norm, scaler=Z.LossScaler(scale=w.loss_scale),
+                      device_state=device_state)
     scaler, t, skips = oracle.LossScalerState(scale=w.loss_scale), 0, []
     last = None
     for it in range(1, w.n_steps + 1):
-        scale = opt.scaler.scale
+        scale = opt.read_state().scaler.scale if device_state else opt.scaler.scale
         assert scale == scaler.scale
         g = W.grad_for_step(w, begin, S, it, scale)
         G.copy_(torch.from_numpy(g.view(np.int16)).view(torch.float16))
         skip = opt.step(G, par)
+        if device_state:
+            skip = bool(opt.read_state().last_overflow)
         ref_sq, ref_ovf = oracle.shard_sqnorm_overflow(g, "f16", 1.0 / scale)
         scaler, ref_skip = oracle.loss_scaler_update(scaler, ref_ovf)
         assert skip == ref_skip and int(opt.overflow.item()) == int(ref_ovf)
@@ -199,17 +200,21 @@ def test_fp32_accumulation_full_shard(Z):
     ref_sq, ref_ovf = oracle.global_sqnorm_overflow(acc_blocks(), "f32", 1.0)
     h = {k: np.concatenate(a) for k, a in host.items()}
     A = torch.empty(S, dtype=torch.float32, device="cuda")
-    for k in range(K):
-        Z.zero_shard_grad_accumulate(A, Gs[k], inv, first=(k == 0))
-    del Gs
-    sq, ovf = _norm(Z, A, 1.0)
     par = torch.empty(S, dtype=torch.bfloat16, device="cuda")
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
               max_grad_norm=w.max_grad_norm, step=w.step, inv_loss_scale=1.0)
-    Z.zero_shard_adam_step(P, M, V, A, par, Z.AdamHyper(**hp), sq, ovf)
-    torch.cuda.synchronize()
-    assert int(ovf.item()) == int(ref_ovf) == 0
-    check_norm(sq.item(), ref_sq)
+    # as bench.py --accum runs it: device step state, the last micro-batch
+    # writing the copy and its norm in one pass
+    opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                      max_grad_norm=w.max_grad_norm, applied_steps=w.step - 1, device_state=True,
+                      scaler=Z.LossScaler.static(w.loss_scale))
+    for k in range(K):
+        opt.accumulate(A, Gs[k], first=(k == 0), last=(k == K - 1))
+    opt.step(A, par, norm_done=True)
+    st = opt.read_state()
+    del Gs
+    assert st.last_overflow == int(ref_ovf) == 0 and st.applied == w.step
+    check_norm(opt.sqnorm.item(), ref_sq)
     idx_t = torch.from_numpy(idx).cuda()
     acc_got = _gather(A, idx_t).cpu().numpy()
     assert (np.abs(acc_got.astype(np.float64) - h["acc"]) <= np.abs(np.spacing(h["acc"]))).all()
