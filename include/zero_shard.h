@@ -128,7 +128,9 @@ int zero_rank_fragments(const int64_t* dims, const int32_t* ndims, int32_t n_ten
  *              bytes (no initial contents needed; clobbered)
  * The grad shard is only read.  Two kernels are enqueued (block partials,
  * then a one-block fixed-order combine).  For n == 0 the outputs are
- * written as 0 by one small kernel.
+ * written as 0 by one small kernel.  The workspace, d_sqnorm and d_overflow
+ * must not overlap one another, and the workspace must not overlap grad
+ * (ZERO_EINVAL).
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ENOSPC (workspace), ZERO_ERANGE,
  * ZERO_EHIP.
  * ------------------------------------------------------------------------- */
@@ -174,7 +176,9 @@ typedef struct {
  * p = p*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps).
  * Streams 28 bytes per element (2 grad + 3x4 read, 3x4 write + 2 param;
  * 30 with an fp32 gradient).
- * grad must not alias master, exp_avg, exp_avg_sq or param_out.
+ * grad must not alias master, exp_avg, exp_avg_sq or param_out, and
+ * d_global_sqnorm / d_global_overflow must not lie in any of those four
+ * (every workgroup reads them while others write the shard): ZERO_EINVAL.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
  * ------------------------------------------------------------------------- */
 int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
@@ -243,7 +247,7 @@ int zero_step_graph_destroy(zero_step_graph* g);
  *              inf/NaN; never cleared by the library (the caller zeroes it
  *              when it wants a per-step flag).  Not needed for skipping: an
  *              inf/NaN propagates into acc, and the norm pass over acc
- *              (grad_dtype ZERO_F32) reports it.
+ *              (grad_dtype ZERO_F32) reports it.  Must not lie in acc.
  * Streams 10 bytes per element (6 for the first micro-batch).
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
  * ------------------------------------------------------------------------- */
@@ -273,7 +277,7 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
  *  n_slices   K, 1 <= K <= ZERO_MAX_SLICES
  *  inv_loss_scale  1 / loss scale (> 0, finite)
  *  d_overflow device int32 or NULL: set to 1 if any slice holds an inf/NaN;
- *             never cleared by the library
+ *             never cleared by the library; must not lie in acc
  * Streams 2K + 4 bytes per element.
  * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
  * ------------------------------------------------------------------------- */
@@ -436,7 +440,9 @@ int zero_step_graph_launch_dev(zero_step_graph* g, void* hip_stream);
  * tasks and blocks in a fixed order: deterministic, but summed in another
  * order than the norm pass, so its last bits may differ from it.
  *  d_workspace  device scratch of zero_sum_norm_workspace_bytes(n) bytes,
- *               16-byte aligned (about n/32 bytes), not overlapping acc
+ *               16-byte aligned (about n/32 bytes), overlapping neither acc,
+ *               a slice, d_sqnorm nor d_overflow; d_sqnorm and d_overflow
+ *               must not overlap each other or lie in acc
  * zero_shard_grad_sum_norm_dev: the same with inv_loss_scale = 1/scale
  *   read from d_state; with hp given (one rank, whose flag is the global
  *   one) its final kernel also makes the step's decision into d_coef, as

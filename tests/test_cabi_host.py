@@ -369,3 +369,38 @@ def test_sum_norm_rejects_bad_arguments_on_host():
              None) == L.ZERO_EINVAL                                      # decision without d_coef
     assert Z.zero_sum_norm_workspace_bytes(-1) == 0
     assert Z.zero_sum_norm_workspace_bytes(976077312) < 976077312 // 16
+
+
+def test_scalar_and_workspace_aliasing_rejected_on_host():
+    """A norm, flag or workspace that lies inside a buffer the same call
+    writes (or reads while another block writes) is rejected before any
+    launch: every layout below overlaps somewhere."""
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    nrm = lib.zero_shard_unscale_norm_overflow
+    need = Z.zero_norm_workspace_bytes(8)
+    assert nrm(al + 1024, L.ZERO_F16, 8, 1.0, al + 512, al + 520, al + 1024, need, None) == L.ZERO_EINVAL   # grad in ws
+    assert nrm(al, L.ZERO_F16, 8, 1.0, al + 1032, al + 520, al + 1024, need, None) == L.ZERO_EINVAL         # sq in ws
+    assert nrm(al, L.ZERO_F16, 8, 1.0, al + 512, al + 1028, al + 1024, need, None) == L.ZERO_EINVAL         # flag in ws
+    assert nrm(al, L.ZERO_F16, 8, 1.0, al + 512, al + 516, al + 1024, need, None) == L.ZERO_EINVAL          # sq over flag
+    assert nrm(al, L.ZERO_F16, 0, 1.0, al + 1024, al + 520, al + 1024, need, None) == L.ZERO_EINVAL         # also at n = 0
+    hp = ctypes.byref(L.zero_adam_params(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 1.0, 0.0))
+    step = lib.zero_shard_adam_step
+    assert step(al, al + 16, al + 32, al + 48, L.ZERO_F16, None, 0, 4, hp, None, al + 4, None) == L.ZERO_EINVAL
+    assert step(al, al + 16, al + 32, al + 48, L.ZERO_F16, None, 0, 4, hp, al + 16, al + 512, None) == L.ZERO_EINVAL
+    assert step(al, al + 16, al + 32, al + 48, L.ZERO_F16, al + 64, L.ZERO_F16, 4, hp, None, al + 68,
+                None) == L.ZERO_EINVAL                                                          # flag in param_out
+    acc = lib.zero_shard_grad_accumulate
+    assert acc(al, al + 16, L.ZERO_F16, 4, 1.0, 1, al + 8, None) == L.ZERO_EINVAL
+    red = lib.zero_shard_grad_reduce
+    one = (ctypes.c_void_p * 1)(al + 256)
+    assert red(al, one, 1, L.ZERO_F16, 4, 1.0, al + 12, None) == L.ZERO_EINVAL
+    sn = lib.zero_shard_grad_sum_norm
+    ws = Z.zero_sum_norm_workspace_bytes(8)
+    assert sn(al, (ctypes.c_void_p * 1)(al + 1024), 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 520, al + 1024, ws,
+              None) == L.ZERO_EINVAL                                                            # slice in ws
+    assert sn(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 1024, al + 520, al + 1024, ws, None) == L.ZERO_EINVAL
+    assert sn(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 8, al + 520, al + 1024, ws, None) == L.ZERO_EINVAL  # sq in acc
+    assert sn(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 20, al + 1024, ws, None) == L.ZERO_EINVAL  # flag in acc
+    assert "lies in" in lib.zero_last_error().decode()

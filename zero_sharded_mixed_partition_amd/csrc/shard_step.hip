@@ -51,6 +51,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <type_traits>
 #include <utility>
 
@@ -808,6 +809,14 @@ int check_step_args(float* master, float* exp_avg, float* exp_avg_sq, const void
         (param_out && (overlaps(param_out, b16, master, b32) || overlaps(param_out, b16, exp_avg, b32) ||
                        overlaps(param_out, b16, exp_avg_sq, b32))))
         return fail(ZERO_EINVAL, "state buffers overlap");
+    // every workgroup reads the flag and the norm while others write the shard
+    for (const auto& sc : {std::make_pair((const void*)d_sq, (int64_t)sizeof(double)),
+                           std::make_pair((const void*)d_ovf, (int64_t)sizeof(int32_t))}) {
+        if (sc.first == nullptr) continue;
+        if (overlaps(sc.first, sc.second, master, b32) || overlaps(sc.first, sc.second, exp_avg, b32) ||
+            overlaps(sc.first, sc.second, exp_avg_sq, b32) || (param_out && overlaps(sc.first, sc.second, param_out, b16)))
+            return fail(ZERO_EINVAL, "d_global_sqnorm / d_global_overflow lies in a buffer the update writes");
+    }
     return ZERO_OK;
 }
 
@@ -844,8 +853,15 @@ int norm_pass(const void* grad, int32_t grad_dtype, int64_t n, double inv2, cons
         return fail(ZERO_EALIGN, "grad and workspace must be 16-byte aligned");
     if (((uintptr_t)d_sqnorm & 7u) || ((uintptr_t)d_overflow & 3u))
         return fail(ZERO_EALIGN, "d_sqnorm / d_overflow misaligned");
-    if (workspace_bytes < zero_norm_workspace_bytes(n))
-        return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, zero_norm_workspace_bytes(n));
+    const size_t need = zero_norm_workspace_bytes(n);
+    if (workspace_bytes < need)
+        return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    if ((n > 0 && overlaps(grad, n * (grad_dtype == ZERO_F32 ? 4 : 2), d_workspace, (int64_t)need)) ||
+        overlaps(d_sqnorm, sizeof(double), d_workspace, (int64_t)need) ||
+        overlaps(d_overflow, sizeof(int32_t), d_workspace, (int64_t)need) ||
+        overlaps(d_sqnorm, sizeof(double), d_overflow, sizeof(int32_t)))
+        return fail(ZERO_EINVAL, "workspace, d_sqnorm and d_overflow must not overlap each other or grad");
     const int nb = norm_blocks(n);
     double* part_sq = static_cast<double*>(d_workspace);
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + nb);
@@ -1049,6 +1065,7 @@ int accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, doub
     if (d_overflow && ((uintptr_t)d_overflow & 3u)) return fail(ZERO_EALIGN, "d_overflow misaligned");
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     if (overlaps(acc, n * 4, grad, n * 2)) return fail(ZERO_EINVAL, "acc aliases grad");
+    if (d_overflow && overlaps(acc, n * 4, d_overflow, sizeof(int32_t))) return fail(ZERO_EINVAL, "d_overflow lies in acc");
     const dim3 grid = elementwise_grid(n);
     const float inv = (float)inv_loss_scale;
 #define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), 0, s, acc, grad, n, inv, \
@@ -1083,6 +1100,7 @@ int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad
         if (overlaps(acc, n * 4, slices[r], n * 2)) return fail(ZERO_EINVAL, "acc aliases slice %d", r);
         sl.p[r] = slices[r];
     }
+    if (d_overflow && overlaps(acc, n * 4, d_overflow, sizeof(int32_t))) return fail(ZERO_EINVAL, "d_overflow lies in acc");
     const dim3 grid = elementwise_grid(n);
     const float inv = (float)inv_loss_scale;
     if (grad_dtype == ZERO_F16) launch_reduce<ZERO_F16>(grid, s, acc, sl, n_slices, n, inv, d_scale, d_overflow);
@@ -1127,15 +1145,22 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     const SumNormLayout l = sum_norm_layout(n);
     if (workspace_bytes < l.bytes) return fail(ZERO_ENOSPC, "workspace %zu bytes, need %zu", workspace_bytes, l.bytes);
+    const int64_t wsb = (int64_t)l.bytes;
+    if (overlaps(d_sqnorm, sizeof(double), d_workspace, wsb) || overlaps(d_overflow, sizeof(int32_t), d_workspace, wsb) ||
+        overlaps(d_sqnorm, sizeof(double), d_overflow, sizeof(int32_t)))
+        return fail(ZERO_EINVAL, "workspace, d_sqnorm and d_overflow must not overlap");
     SlicesOf<ZERO_MAX_SLICES> sl{};
     if (n > 0) {
         if (acc == nullptr || slices == nullptr) return fail(ZERO_EINVAL, "NULL acc or slices");
         if (!aligned16(acc)) return fail(ZERO_EALIGN, "acc must be 16-byte aligned");
-        if (overlaps(acc, n * 4, d_workspace, (int64_t)workspace_bytes)) return fail(ZERO_EINVAL, "acc aliases workspace");
+        if (overlaps(acc, n * 4, d_workspace, wsb)) return fail(ZERO_EINVAL, "acc aliases workspace");
+        if (overlaps(acc, n * 4, d_sqnorm, sizeof(double)) || overlaps(acc, n * 4, d_overflow, sizeof(int32_t)))
+            return fail(ZERO_EINVAL, "d_sqnorm / d_overflow lies in acc");
         for (int32_t r = 0; r < n_slices; ++r) {
             if (slices[r] == nullptr) return fail(ZERO_EINVAL, "slice %d is NULL", r);
             if (!aligned16(slices[r])) return fail(ZERO_EALIGN, "slice %d must be 16-byte aligned", r);
             if (overlaps(acc, n * 4, slices[r], n * 2)) return fail(ZERO_EINVAL, "acc aliases slice %d", r);
+            if (overlaps(slices[r], n * 2, d_workspace, wsb)) return fail(ZERO_EINVAL, "slice %d aliases workspace", r);
             sl.p[r] = slices[r];
         }
     }
