@@ -43,6 +43,7 @@ def test_sum_norm_matches_separate_kernels_and_oracle(Z, n, k, add, fmt):
     B = to_device(base) if add else torch.empty(n, device="cuda")
     sq, ovf = _scalars()
     ws = torch.empty(Z.zero_sum_norm_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)              # NaN bytes: a partial slot that is read but never written shows as overflow
     Z.zero_shard_grad_sum_norm(A, D, add, inv, sq, ovf, ws)
     if add:
         for d in D:

@@ -94,6 +94,12 @@ constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per
 // The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
 // peak with no reservation against 45-63% with the 12 KiB cap.
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
+// gfx950 has 8 XCDs, each with its own L2; consecutive workgroups of a launch
+// go to them in turn.  Small per-workgroup results that neighbouring
+// workgroups write into one array are laid out XCD by XCD (slot of task t:
+// (t % kXcds) * per_xcd + t / kXcds) so each L2 fills whole lines instead of
+// eight L2s writing back the same lines sector by sector.
+constexpr int kXcds = 8;
 
 // ---------------------------------------------------------------- gradient formats
 
@@ -645,14 +651,15 @@ __device__ __forceinline__ double wave_sum(double v) {
 // acc = (ADD ? acc : 0) + sum_k slice_k * inv in slice order (the same
 // operations as grad_accumulate / grad_reduce), and, per one-wave task, the
 // fp64 sum of the squares of the 256 results it wrote: one partial per task
-// in part_task, summed over the wave in a fixed order (wave_sum).  A
+// in part_task (at task t's XCD-major slot, per_xcd slots per XCD), summed
+// over the wave in a fixed order (wave_sum).  A
 // non-finite result makes its partial non-finite (the square of a finite
 // fp32 value, and any sum of up to 2^40 of them, stays finite in fp64), so
 // the overflow flag is read off the partials.
 template <int DT, bool ADD, int MAXK>
 __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ A, SlicesOf<MAXK> sl, int k, int64_t n,
                                                             float inv, const double* __restrict__ d_scale,
-                                                            double* __restrict__ part_task) {
+                                                            double* __restrict__ part_task, int64_t per_xcd) {
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     const int lane = threadIdx.x;
     const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
@@ -696,22 +703,31 @@ __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ 
             }
         }
         sq = wave_sum(sq);
-        if (lane == 0) st_stream(sq, part_task + t);        // read once, by task_partials_reduce
+        // a cached store: neighbouring tasks' 8-byte partials merge into whole
+        // lines in L2 (with the non-temporal hint each went to HBM as a
+        // partial-line write)
+        if (lane == 0) part_task[(t % kXcds) * per_xcd + t / kXcds] = sq;
     }
 }
 
 // The task partials into at most kNormMaxBlocks block partials: block b sums
-// its contiguous range of tasks in a fixed order; bad = any non-finite partial.
+// its contiguous range of slots in a fixed order, skipping the slots no task
+// maps to (the last slot of an XCD when kXcds does not divide ntasks); bad =
+// any non-finite partial.
 __global__ __launch_bounds__(kBlock) void task_partials_reduce(const double* __restrict__ part_task, int64_t ntasks,
-                                                               int64_t per_block, double* __restrict__ part_sq,
+                                                               int64_t per_xcd, int64_t per_block,
+                                                               double* __restrict__ part_sq,
                                                                uint32_t* __restrict__ part_bad) {
     __shared__ double s_sq[kWaves];
     __shared__ uint32_t s_bad[kWaves];
+    const int64_t nslots = per_xcd * kXcds;
     const int64_t lo = (int64_t)blockIdx.x * per_block;
-    const int64_t hi = lo + per_block < ntasks ? lo + per_block : ntasks;
+    const int64_t hi = lo + per_block < nslots ? lo + per_block : nslots;
     double acc = 0.0;
     uint32_t bad = 0;
     for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+        const int64_t xcd = i / per_xcd;
+        if ((i - xcd * per_xcd) * kXcds + xcd >= ntasks) continue;     // no task writes this slot
         const double x = part_task[i];
         bad |= ((__double_as_longlong(x) >> 52) & 0x7FF) == 0x7FF ? 1u : 0u;
         acc += x;
@@ -1030,9 +1046,9 @@ SlicesOf<MAXK> first_slices(const SlicesOf<ZERO_MAX_SLICES>& sl) {
 
 template <int DT, bool ADD>
 void launch_sum_norm(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
-                     float inv, const double* d_scale, double* part_task) {
+                     float inv, const double* d_scale, double* part_task, int64_t per_xcd) {
 #define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), 0, s, acc, \
-                                     first_slices<M>(sl), (int)k, n, inv, d_scale, part_task)
+                                     first_slices<M>(sl), (int)k, n, inv, d_scale, part_task, per_xcd)
     if (k <= 1) ZS_SUM(1);
     else if (k <= 2) ZS_SUM(2);
     else if (k <= 4) ZS_SUM(4);
@@ -1108,10 +1124,12 @@ int reduce(float* acc, const void* const* slices, int32_t n_slices, int32_t grad
     return launch_status("grad_reduce");
 }
 
-// Layout of the fused pass's workspace: one double per task, then the block
-// partials of the norm pass (double, uint32).
+// Layout of the fused pass's workspace: kXcds * per_xcd task slots (one
+// double per task, XCD-major), then the block partials of the norm pass
+// (double, uint32).
 struct SumNormLayout {
     int64_t ntasks;
+    int64_t per_xcd;
     int nb;
     int64_t per_block;
     size_t bytes;
@@ -1120,12 +1138,14 @@ struct SumNormLayout {
 SumNormLayout sum_norm_layout(int64_t n) {
     SumNormLayout l;
     l.ntasks = (n + kEwTask - 1) / kEwTask;
+    l.per_xcd = (l.ntasks + kXcds - 1) / kXcds;
+    const int64_t nslots = l.per_xcd * kXcds;
     int64_t nb = l.ntasks / 1024;
     if (nb < 1) nb = 1;
     if (nb > kNormMaxBlocks) nb = kNormMaxBlocks;
     l.nb = (int)nb;
-    l.per_block = (l.ntasks + nb - 1) / nb;
-    const size_t raw = (size_t)(l.ntasks + nb) * sizeof(double) + (size_t)nb * sizeof(uint32_t);
+    l.per_block = (nslots + nb - 1) / nb;
+    const size_t raw = (size_t)(nslots + nb) * sizeof(double) + (size_t)nb * sizeof(uint32_t);
     l.bytes = (raw + 255) & ~(size_t)255;
     return l;
 }
@@ -1165,23 +1185,23 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
         }
     }
     double* part_task = static_cast<double*>(d_workspace);
-    double* part_sq = part_task + l.ntasks;
+    double* part_sq = part_task + l.per_xcd * kXcds;
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + l.nb);
     int nparts = 0;
     if (n > 0) {
         const dim3 grid = elementwise_grid(n);
         const float inv = (float)inv_loss_scale;
         if (grad_dtype == ZERO_F16) {
-            if (add) launch_sum_norm<ZERO_F16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
-            else launch_sum_norm<ZERO_F16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
+            if (add) launch_sum_norm<ZERO_F16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task, l.per_xcd);
+            else launch_sum_norm<ZERO_F16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task, l.per_xcd);
         } else {
-            if (add) launch_sum_norm<ZERO_BF16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
-            else launch_sum_norm<ZERO_BF16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task);
+            if (add) launch_sum_norm<ZERO_BF16, true>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task, l.per_xcd);
+            else launch_sum_norm<ZERO_BF16, false>(grid, s, acc, sl, n_slices, n, inv, d_scale, part_task, l.per_xcd);
         }
         int st = launch_status("grad_sum_norm");
         if (st != ZERO_OK) return st;
-        hipLaunchKernelGGL(task_partials_reduce, dim3(l.nb), dim3(kBlock), 0, s, part_task, l.ntasks, l.per_block,
-                           part_sq, part_bad);
+        hipLaunchKernelGGL(task_partials_reduce, dim3(l.nb), dim3(kBlock), 0, s, part_task, l.ntasks, l.per_xcd,
+                           l.per_block, part_sq, part_bad);
         st = launch_status("task_partials_reduce");
         if (st != ZERO_OK) return st;
         nparts = l.nb;
