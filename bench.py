@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,9 +40,18 @@ KERNEL_SRC = os.path.join(ROOT, "zero_sharded_mixed_partition_amd", "csrc", "sha
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
+def code_hash(text: str) -> str:
+    """sha256[:16] of C/HIP source with its comments and blank lines removed,
+    so that the counter summaries stay tied to the code, not to its comments."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        return code_hash(f.read())
 
 
 def measured_traffic(key: str, kernel: str = "adam_update"):
@@ -54,7 +64,7 @@ def measured_traffic(key: str, kernel: str = "adam_update"):
     except (OSError, ValueError):
         return None
     rec = data.get(kernel, {}).get(key)
-    if not rec or rec.get("kernel_sha256_16") != kernel_source_hash():
+    if not rec or rec.get("kernel_code_sha256_16") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 

@@ -21,7 +21,16 @@ def test_counter_summary_is_tied_to_kernel_source():
     rec = data["adam_update"]["gpt_1t_nd1024_last_rank"]
     # the algorithmic bytes recorded with the counters are 28 B/param of the shard
     assert rec["algorithmic_bytes"] == 28 * 976077312
-    if rec["kernel_sha256_16"] == bench.kernel_source_hash():
+    if rec["kernel_code_sha256_16"] == bench.kernel_source_hash():
         assert bench.measured_traffic("gpt_1t_nd1024_last_rank") == rec["bytes_per_launch"]
     else:
         assert bench.measured_traffic("gpt_1t_nd1024_last_rank") is None
+
+
+def test_code_hash_ignores_comments_only():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = "int f(int x) {\n    return x + 1;  // one more\n}\n"
+    b = "/* header */\nint f(int x) {\n\n    return x + 1;  // a different comment\n}\n"
+    c = "int f(int x) {\n    return x + 2;  // one more\n}\n"
+    assert bench.code_hash(a) == bench.code_hash(b) != bench.code_hash(c)

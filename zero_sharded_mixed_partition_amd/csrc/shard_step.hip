@@ -703,9 +703,8 @@ __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ 
             }
         }
         sq = wave_sum(sq);
-        // a cached store: neighbouring tasks' 8-byte partials merge into whole
-        // lines in L2 (with the non-temporal hint each went to HBM as a
-        // partial-line write)
+        // a cached store into this XCD's run of slots: the 8-byte partials of
+        // the tasks one XCD runs fill whole lines of its L2 before write-back
         if (lane == 0) part_task[(t % kXcds) * per_xcd + t / kXcds] = sq;
     }
 }
