@@ -93,6 +93,12 @@ constexpr int kAdamTasks = 1;
 constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per workgroup
 // The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
 // peak with no reservation against 45-63% with the 12 KiB cap.
+// The fused copy-and-norm pass compiled for 5-8 slices (nine or ten streams)
+// gains from a light cap: 6 KiB per one-wave workgroup (26 resident per CU
+// instead of 32) took 8 slices on a 976M-element shard from 6.47 to 6.60
+// TB/s; 8 KiB and more lose 10-45%.  Capacities 1-4 and 16 are fastest, or
+// within noise, uncapped.
+constexpr size_t kSumNormLds8 = 6 * 1024;
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
 // gfx950 has 8 XCDs, each with its own L2; consecutive workgroups of a launch
 // go to them in turn.  Small per-workgroup results that neighbouring
@@ -660,6 +666,10 @@ template <int DT, bool ADD, int MAXK>
 __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ A, SlicesOf<MAXK> sl, int k, int64_t n,
                                                             float inv, const double* __restrict__ d_scale,
                                                             double* __restrict__ part_task, int64_t per_xcd) {
+    // dynamic LDS reserved by the launcher for capacity 8 only, to cap
+    // residency; never read
+    extern __shared__ float occupancy_pad[];
+    if (n < 0) occupancy_pad[threadIdx.x] = 0.0f;
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     const int lane = threadIdx.x;
     const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
@@ -1046,7 +1056,7 @@ SlicesOf<MAXK> first_slices(const SlicesOf<ZERO_MAX_SLICES>& sl) {
 template <int DT, bool ADD>
 void launch_sum_norm(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
                      float inv, const double* d_scale, double* part_task, int64_t per_xcd) {
-#define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), 0, s, acc, \
+#define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), (M) == 8 ? kSumNormLds8 : 0, s, acc, \
                                      first_slices<M>(sl), (int)k, n, inv, d_scale, part_task, per_xcd)
     if (k <= 1) ZS_SUM(1);
     else if (k <= 2) ZS_SUM(2);
