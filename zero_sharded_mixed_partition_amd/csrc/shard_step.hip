@@ -93,12 +93,13 @@ constexpr int kAdamTasks = 1;
 constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per workgroup
 // The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
 // peak with no reservation against 45-63% with the 12 KiB cap.
-// The fused copy-and-norm pass compiled for 5-8 slices (nine or ten streams)
-// gains from a light cap: 6 KiB per one-wave workgroup (26 resident per CU
-// instead of 32) took 8 slices on a 976M-element shard from 6.47 to 6.60
-// TB/s; 8 KiB and more lose 10-45%.  Capacities 1-4 and 16 are fastest, or
-// within noise, uncapped.
-constexpr size_t kSumNormLds8 = 6 * 1024;
+// The reduction and the fused copy-and-norm pass compiled for 5-8 slices
+// (nine or ten streams) gain from a light cap: 6 KiB per one-wave workgroup
+// (26 resident per CU instead of 32) took 8 slices on a 976M-element shard
+// from 6.49 to 6.63 TB/s (reduction) and from 6.47 to 6.60 TB/s (fused);
+// 8 KiB and more lose 10-45%.  Capacities 1-4 and 16, and the accumulation
+// kernels, are fastest, or within noise, uncapped.
+constexpr size_t kSlices8Lds = 6 * 1024;
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
 // gfx950 has 8 XCDs, each with its own L2; consecutive workgroups of a launch
 // go to them in turn.  Small per-workgroup results that neighbouring
@@ -578,6 +579,10 @@ template <int DT, int MAXK>
 __global__ __launch_bounds__(kEwThreads) void grad_reduce(float* __restrict__ A, SlicesOf<MAXK> sl, int k, int64_t n,
                                                           float inv, const double* __restrict__ d_scale,
                                                           int32_t* __restrict__ d_ovf) {
+    // dynamic LDS reserved by the launcher for capacity 8 only, to cap
+    // residency; never read
+    extern __shared__ float occupancy_pad[];
+    if (n < 0) occupancy_pad[threadIdx.x] = 0.0f;
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     uint32_t bad = 0;
     const int lane = threadIdx.x;
@@ -1056,7 +1061,7 @@ SlicesOf<MAXK> first_slices(const SlicesOf<ZERO_MAX_SLICES>& sl) {
 template <int DT, bool ADD>
 void launch_sum_norm(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
                      float inv, const double* d_scale, double* part_task, int64_t per_xcd) {
-#define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), (M) == 8 ? kSumNormLds8 : 0, s, acc, \
+#define ZS_SUM(M) hipLaunchKernelGGL((grad_sum_norm<DT, ADD, M>), grid, dim3(kEwThreads), (M) == 8 ? kSlices8Lds : 0, s, acc, \
                                      first_slices<M>(sl), (int)k, n, inv, d_scale, part_task, per_xcd)
     if (k <= 1) ZS_SUM(1);
     else if (k <= 2) ZS_SUM(2);
@@ -1069,7 +1074,7 @@ void launch_sum_norm(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_M
 template <int DT>
 void launch_reduce(dim3 grid, hipStream_t s, float* acc, const SlicesOf<ZERO_MAX_SLICES>& sl, int32_t k, int64_t n,
                    float inv, const double* d_scale, int32_t* d_overflow) {
-#define ZS_RED(M) hipLaunchKernelGGL((grad_reduce<DT, M>), grid, dim3(kEwThreads), 0, s, acc, first_slices<M>(sl), \
+#define ZS_RED(M) hipLaunchKernelGGL((grad_reduce<DT, M>), grid, dim3(kEwThreads), (M) == 8 ? kSlices8Lds : 0, s, acc, first_slices<M>(sl), \
                                      (int)k, n, inv, d_scale, d_overflow)
     if (k <= 1) ZS_RED(1);
     else if (k <= 2) ZS_RED(2);
