@@ -346,7 +346,7 @@ int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip
  *
  * zero_step_state: 72 bytes, device memory, 8-byte aligned, initialised by
  * the caller (a valid scaler as for zero_loss_scaler_update; applied = the
- * steps already applied; skipped, last_overflow, arrivals = 0).
+ * steps already applied; skipped, last_overflow, reserved = 0).
  *
  * zero_shard_unscale_norm_overflow_dev: zero_shard_unscale_norm_overflow
  *   with inv_loss_scale = 1/scale read from d_state when the kernel runs
@@ -382,9 +382,7 @@ typedef struct {
     int64_t applied;               /* steps applied so far; the next step has t = applied + 1 */
     int64_t skipped;               /* steps skipped on overflow so far */
     int32_t last_overflow;         /* the last step's global overflow flag */
-    int32_t arrivals;              /* workgroup arrival count of the calls that end their norm pass in
-                                      the last workgroup (zero_shard_norm_decide_dev,
-                                      zero_shard_grad_sum_norm_dev): 0 at creation, left 0 by every call */
+    int32_t reserved;
 } zero_step_state;
 
 int zero_shard_unscale_norm_overflow_dev(const void* grad, int32_t grad_dtype, int64_t n,

@@ -148,7 +148,7 @@ def test_device_state_graph_replays_match_eager(Z, wname, n):
         recorded.append(graph.recorded_this_step)
         se, sg = eager.read_state(), graph.read_state()
         assert bytes(se) == bytes(sg), f"iteration {it}"
-        assert sg.last_overflow == (it == 3) and sg.arrivals == 0
+        assert sg.last_overflow == (it == 3)
         for a, b in ((eager.master, graph.master), (eager.exp_avg, graph.exp_avg),
                      (eager.exp_avg_sq, graph.exp_avg_sq)):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"iteration {it}"

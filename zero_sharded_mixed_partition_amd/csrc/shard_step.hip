@@ -252,6 +252,53 @@ __device__ __forceinline__ void accumulate_vec(u32x4 q, double& acc, uint32_t& b
     }
 }
 
+// Grid-stride over chunks of kChunk consecutive 16-byte vectors: at every
+// step the grid reads one contiguous window, and each wave's four loads are
+// consecutive 1 KiB runs.  The grid size depends only on n, so the summation
+// order (and the result) is the same on every run.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restrict__ g, int64_t nvec,
+                                                          const void* __restrict__ tail, int tail_n,
+                                                          double* __restrict__ part_sq,
+                                                          uint32_t* __restrict__ part_bad) {
+    __shared__ double s_sq[kWaves];
+    __shared__ uint32_t s_bad[kWaves];
+    double acc = 0.0;
+    uint32_t bad = 0;
+    constexpr int kUnroll = GradFmt<DT>::norm_unroll;
+    constexpr int64_t kChunk = (int64_t)kBlock * kUnroll;
+    const int64_t nchunks = nvec / kChunk;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const u32x4* base = g + c * kChunk + threadIdx.x;
+        u32x4 q[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) q[u] = ld_stream(base + u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
+    }
+    if (blockIdx.x == 0) {
+        // fewer than kChunk vectors left over, then less than one vector
+        for (int64_t i = nchunks * kChunk + threadIdx.x; i < nvec; i += kBlock)
+            accumulate_vec<DT>(ld_stream(g + i), acc, bad);
+        if (threadIdx.x == 0) {
+            for (int k = 0; k < tail_n; ++k) {
+                uint32_t w;
+                if constexpr (DT == ZERO_F32) w = static_cast<const uint32_t*>(tail)[k];
+                else w = static_cast<const uint16_t*>(tail)[k];
+                bad |= (w & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                const double a = (double)load_grad1<DT>(tail, k);
+                acc = fma(a, a, acc);
+            }
+        }
+    }
+    bad = (bad & kNonfiniteBits) != 0;
+    block_reduce(acc, bad, s_sq, s_bad);
+    if (threadIdx.x == 0) {
+        part_sq[blockIdx.x] = acc;
+        part_bad[blockIdx.x] = bad;
+    }
+}
+
 // ---------------------------------------------------------------- device-resident step state
 
 struct HyperArgs {
@@ -291,28 +338,20 @@ __global__ __launch_bounds__(64) void step_decide(zero_step_state* __restrict__ 
     if (threadIdx.x == 0) decide_step(st, *d_ovf != 0 ? 1 : 0, h, unscaled_grad, coef);
 }
 
-// How a norm pass ends: the factor on the raw sum of squares is (1/scale)^2,
-// read from d_scale or, if NULL, inv2 by value; with st_decide set (a single
-// rank, whose flag is the global one) the step's decision follows.  With
-// st_count set, the partial kernel's last workgroup to arrive does this
-// itself instead of a separate one-block kernel (the arrival counter lives in
-// that step state, which must be 0 at creation and is left 0).
-struct NormFinish {
-    zero_step_state* st_count;
-    zero_step_state* st_decide;
-    const double* d_scale;
-    double* d_sq;
-    int32_t* d_ovf;
-    StepCoef* coef;
-    double inv2;
-    HyperArgs h;
-    int unscaled_grad;
-};
-
-// One block: the fixed-order sum and OR of the nparts partials, then the
-// outputs and, for a single rank, the decision (thread 0).
-__device__ void finalize_norm(const double* __restrict__ part_sq, const uint32_t* __restrict__ part_bad, int nparts,
-                              const NormFinish& f, double* s_sq, uint32_t* s_bad) {
+// d_scale (device loss scale) or, if NULL, inv2 by value: the factor applied
+// to the raw sum of squares is (1/scale)^2.
+// With st_decide set (a single rank, whose flag is the global one), thread 0
+// also makes the step's decision (decide_step) from the flag it just formed.
+__global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restrict__ part_sq,
+                                                          const uint32_t* __restrict__ part_bad,
+                                                          int nparts, double inv2,
+                                                          const double* __restrict__ d_scale,
+                                                          double* __restrict__ d_sq,
+                                                          int32_t* __restrict__ d_ovf,
+                                                          zero_step_state* __restrict__ st_decide, HyperArgs h,
+                                                          int unscaled_grad, StepCoef* __restrict__ coef) {
+    __shared__ double s_sq[kWaves];
+    __shared__ uint32_t s_bad[kWaves];
     double acc = 0.0;
     uint32_t bad = 0;
     for (int i = threadIdx.x; i < nparts; i += kBlock) {
@@ -321,89 +360,14 @@ __device__ void finalize_norm(const double* __restrict__ part_sq, const uint32_t
     }
     block_reduce(acc, bad, s_sq, s_bad);
     if (threadIdx.x == 0) {
-        double inv2 = f.inv2;
-        if (f.d_scale != nullptr) {
-            const double inv = 1.0 / *f.d_scale;
+        if (d_scale != nullptr) {
+            const double inv = 1.0 / *d_scale;
             inv2 = inv * inv;
         }
-        *f.d_sq = acc * inv2;
-        *f.d_ovf = bad ? 1 : 0;
-        if (f.st_decide != nullptr) decide_step(f.st_decide, bad ? 1 : 0, f.h, f.unscaled_grad, f.coef);
+        *d_sq = acc * inv2;
+        *d_ovf = bad ? 1 : 0;
+        if (st_decide != nullptr) decide_step(st_decide, bad ? 1 : 0, h, unscaled_grad, coef);
     }
-}
-
-// Called by every thread of a partial-writing block once its partial is
-// stored: the block that arrives last (device-scope fences around the
-// counter, so every other block's partial is visible to it) finalizes.  No
-// block waits for another.
-__device__ void finish_if_last(const NormFinish& f, const double* __restrict__ part_sq,
-                               const uint32_t* __restrict__ part_bad, int nparts, double* s_sq, uint32_t* s_bad) {
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-        __threadfence();                                 // this block's partial, before its arrival
-        s_last = atomicAdd(&f.st_count->arrivals, 1) == nparts - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                                     // the other blocks' partials, after theirs
-    finalize_norm(part_sq, part_bad, nparts, f, s_sq, s_bad);
-    if (threadIdx.x == 0) f.st_count->arrivals = 0;      // ready for the next call on this state
-}
-
-__global__ __launch_bounds__(kBlock) void sqnorm_finalize(const double* __restrict__ part_sq,
-                                                          const uint32_t* __restrict__ part_bad,
-                                                          int nparts, NormFinish f) {
-    __shared__ double s_sq[kWaves];
-    __shared__ uint32_t s_bad[kWaves];
-    finalize_norm(part_sq, part_bad, nparts, f, s_sq, s_bad);
-}
-
-// Grid-stride over chunks of kChunk consecutive 16-byte vectors: at every
-// step the grid reads one contiguous window, and each wave's four loads are
-// consecutive 1 KiB runs.  The grid size depends only on n, so the summation
-// order (and the result) is the same on every run.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void sqnorm_partials(const u32x4* __restrict__ g, int64_t nvec,
-                                                          const void* __restrict__ tail, int tail_n,
-                                                          double* __restrict__ part_sq,
-                                                          uint32_t* __restrict__ part_bad, NormFinish f) {
-    __shared__ double s_sq[kWaves];
-    __shared__ uint32_t s_bad[kWaves];
-    double acc = 0.0;
-    uint32_t bad = 0;
-    constexpr int kUnroll = GradFmt<DT>::norm_unroll;
-    constexpr int64_t kChunk = (int64_t)kBlock * kUnroll;
-    const int64_t nchunks = nvec / kChunk;
-    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const u32x4* base = g + c * kChunk + threadIdx.x;
-        u32x4 q[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) q[u] = ld_stream(base + u * kBlock);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) accumulate_vec<DT>(q[u], acc, bad);
-    }
-    if (blockIdx.x == 0) {
-        // fewer than kChunk vectors left over, then less than one vector
-        for (int64_t i = nchunks * kChunk + threadIdx.x; i < nvec; i += kBlock)
-            accumulate_vec<DT>(ld_stream(g + i), acc, bad);
-        if (threadIdx.x == 0) {
-            for (int k = 0; k < tail_n; ++k) {
-                uint32_t w;
-                if constexpr (DT == ZERO_F32) w = static_cast<const uint32_t*>(tail)[k];
-                else w = static_cast<const uint16_t*>(tail)[k];
-                bad |= (w & GradFmt<DT>::mask) + GradFmt<DT>::carry;
-                const double a = (double)load_grad1<DT>(tail, k);
-                acc = fma(a, a, acc);
-            }
-        }
-    }
-    bad = (bad & kNonfiniteBits) != 0;
-    block_reduce(acc, bad, s_sq, s_bad);
-    if (threadIdx.x == 0) {
-        part_sq[blockIdx.x] = acc;
-        part_bad[blockIdx.x] = bad;
-    }
-    if (f.st_count != nullptr) finish_if_last(f, part_sq, part_bad, gridDim.x, s_sq, s_bad);
 }
 
 // blocks for a gradient of n elements: one per full block step (8K elements
@@ -767,7 +731,7 @@ __global__ __launch_bounds__(kEwThreads) void grad_sum_norm(float* __restrict__ 
 __global__ __launch_bounds__(kBlock) void task_partials_reduce(const double* __restrict__ part_task, int64_t ntasks,
                                                                int64_t per_xcd, int64_t per_block,
                                                                double* __restrict__ part_sq,
-                                                               uint32_t* __restrict__ part_bad, NormFinish f) {
+                                                               uint32_t* __restrict__ part_bad) {
     __shared__ double s_sq[kWaves];
     __shared__ uint32_t s_bad[kWaves];
     const int64_t nslots = per_xcd * kXcds;
@@ -787,7 +751,6 @@ __global__ __launch_bounds__(kBlock) void task_partials_reduce(const double* __r
         part_sq[blockIdx.x] = acc;
         part_bad[blockIdx.x] = bad;
     }
-    if (f.st_count != nullptr) finish_if_last(f, part_sq, part_bad, gridDim.x, s_sq, s_bad);
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -814,13 +777,12 @@ dim3 elementwise_grid(int64_t n, int64_t per_group = kEwTask) {
 }
 
 template <int DT>
-void launch_norm(int nb, hipStream_t s, const void* grad, int64_t n, double* part_sq, uint32_t* part_bad,
-                 const NormFinish& f) {
+void launch_norm(int nb, hipStream_t s, const void* grad, int64_t n, double* part_sq, uint32_t* part_bad) {
     const int64_t nvec = n / GradFmt<DT>::per_vec;
     const int tail_n = (int)(n - nvec * GradFmt<DT>::per_vec);
     const void* tail = static_cast<const char*>(grad) + nvec * 16;
     hipLaunchKernelGGL(sqnorm_partials<DT>, dim3(nb), dim3(kBlock), 0, s, static_cast<const u32x4*>(grad), nvec,
-                       tail, tail_n, part_sq, part_bad, f);
+                       tail, tail_n, part_sq, part_bad);
 }
 
 // d_coef == nullptr: coefficients c by value; otherwise read from d_coef on the device
@@ -908,12 +870,9 @@ namespace zero_shard {
 namespace {
 
 // The norm pass; the (1/scale)^2 factor is inv2 by value, or read from d_scale.
-// With st_count (a mutable step state) the partial kernel's last block
-// finalizes; otherwise a one-block kernel does.
 int norm_pass(const void* grad, int32_t grad_dtype, int64_t n, double inv2, const double* d_scale, double* d_sqnorm,
               int32_t* d_overflow, void* d_workspace, size_t workspace_bytes, hipStream_t s,
-              zero_step_state* st_decide = nullptr, const HyperArgs& h = HyperArgs{}, StepCoef* coef = nullptr,
-              zero_step_state* st_count = nullptr) {
+              zero_step_state* st_decide = nullptr, const HyperArgs& h = HyperArgs{}, StepCoef* coef = nullptr) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
     if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
         return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
@@ -936,16 +895,15 @@ int norm_pass(const void* grad, int32_t grad_dtype, int64_t n, double inv2, cons
     const int nb = norm_blocks(n);
     double* part_sq = static_cast<double*>(d_workspace);
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + nb);
-    NormFinish f{n > 0 ? st_count : nullptr, st_decide, d_scale, d_sqnorm, d_overflow, coef, inv2, h,
-                 grad_dtype == ZERO_F32 ? 1 : 0};
     if (n > 0) {
-        if (grad_dtype == ZERO_F16) launch_norm<ZERO_F16>(nb, s, grad, n, part_sq, part_bad, f);
-        else if (grad_dtype == ZERO_BF16) launch_norm<ZERO_BF16>(nb, s, grad, n, part_sq, part_bad, f);
-        else launch_norm<ZERO_F32>(nb, s, grad, n, part_sq, part_bad, f);
+        if (grad_dtype == ZERO_F16) launch_norm<ZERO_F16>(nb, s, grad, n, part_sq, part_bad);
+        else if (grad_dtype == ZERO_BF16) launch_norm<ZERO_BF16>(nb, s, grad, n, part_sq, part_bad);
+        else launch_norm<ZERO_F32>(nb, s, grad, n, part_sq, part_bad);
         const int st = launch_status("sqnorm_partials");
-        if (st != ZERO_OK || f.st_count != nullptr) return st;
+        if (st != ZERO_OK) return st;
     }
-    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, n > 0 ? nb : 0, f);
+    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, n > 0 ? nb : 0, inv2, d_scale,
+                       d_sqnorm, d_overflow, st_decide, h, grad_dtype == ZERO_F32 ? 1 : 0, coef);
     return launch_status("sqnorm_finalize");
 }
 
@@ -1041,7 +999,7 @@ int zero_shard_norm_decide_dev(const void* grad, int32_t grad_dtype, int64_t n, 
     const HyperArgs h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_grad_norm};
     const double* d_scale = grad_dtype == ZERO_F32 ? nullptr : &d_state->scaler.scale;
     return norm_pass(grad, grad_dtype, n, 1.0, d_scale, d_sqnorm, d_overflow, d_workspace, workspace_bytes,
-                     static_cast<hipStream_t>(hip_stream), d_state, h, static_cast<StepCoef*>(d_coef), d_state);
+                     static_cast<hipStream_t>(hip_stream), d_state, h, static_cast<StepCoef*>(d_coef));
 }
 
 int zero_step_decide_dev(const zero_adam_hyper* hp, int32_t grad_dtype, zero_step_state* d_state,
@@ -1208,8 +1166,7 @@ SumNormLayout sum_norm_layout(int64_t n) {
 
 int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t grad_dtype, int64_t n, int32_t add,
              double inv_loss_scale, const double* d_scale, double* d_sqnorm, int32_t* d_overflow, void* d_workspace,
-             size_t workspace_bytes, hipStream_t s, zero_step_state* st_decide, const HyperArgs& h, StepCoef* coef,
-             zero_step_state* st_count = nullptr) {
+             size_t workspace_bytes, hipStream_t s, zero_step_state* st_decide, const HyperArgs& h, StepCoef* coef) {
     if (n < 0) return fail(ZERO_EINVAL, "n < 0");
     if (n_slices < 1 || n_slices > ZERO_MAX_SLICES)
         return fail(ZERO_EINVAL, "n_slices must lie in [1, %d] (got %d)", ZERO_MAX_SLICES, n_slices);
@@ -1245,8 +1202,6 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
     double* part_sq = part_task + l.per_xcd * kXcds;
     uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sq + l.nb);
     int nparts = 0;
-    // the copy is already unscaled: the factor on the sum of squares is 1
-    NormFinish f{n > 0 ? st_count : nullptr, st_decide, nullptr, d_sqnorm, d_overflow, coef, 1.0, h, 1};
     if (n > 0) {
         const dim3 grid = elementwise_grid(n);
         const float inv = (float)inv_loss_scale;
@@ -1260,12 +1215,14 @@ int sum_norm(float* acc, const void* const* slices, int32_t n_slices, int32_t gr
         int st = launch_status("grad_sum_norm");
         if (st != ZERO_OK) return st;
         hipLaunchKernelGGL(task_partials_reduce, dim3(l.nb), dim3(kBlock), 0, s, part_task, l.ntasks, l.per_xcd,
-                           l.per_block, part_sq, part_bad, f);
+                           l.per_block, part_sq, part_bad);
         st = launch_status("task_partials_reduce");
-        if (st != ZERO_OK || f.st_count != nullptr) return st;
+        if (st != ZERO_OK) return st;
         nparts = l.nb;
     }
-    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, nparts, f);
+    // the copy is already unscaled: the factor on the sum of squares is 1
+    hipLaunchKernelGGL(sqnorm_finalize, dim3(1), dim3(kBlock), 0, s, part_sq, part_bad, nparts, 1.0, nullptr, d_sqnorm,
+                       d_overflow, st_decide, h, 1, coef);
     return launch_status("sqnorm_finalize");
 }
 
@@ -1343,7 +1300,7 @@ int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t 
     }
     return sum_norm(acc, slices, n_slices, grad_dtype, n, add_to_acc, 1.0, &d_state->scaler.scale, d_sqnorm,
                     d_overflow, d_workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream),
-                    hp != nullptr ? d_state : nullptr, h, static_cast<StepCoef*>(d_coef), d_state);
+                    hp != nullptr ? d_state : nullptr, h, static_cast<StepCoef*>(d_coef));
 }
 
 // ---------------------------------------------------------------- step graphs
