@@ -471,6 +471,31 @@ int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t 
  * ------------------------------------------------------------------------- */
 int zero_copy_reference(void* dst, const void* src, int64_t bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * The local half of the all-reduce of the norm pass's two scalars: the one
+ * exchange inside the step.  Each rank updates only its own partition (ZeRO
+ * method entry, description; explainer, Ch.02 "The Three Stages", what each
+ * stage shards), while the clip coefficient and the skip depend on the whole
+ * gradient: the data-parallel sum of the ranks' sums of squares and the OR of
+ * their inf/NaN flags.  With a direct exchange every rank writes its
+ * (d_sqnorm, d_overflow) into slot r of two arrays on every peer; once the
+ * slots have landed, each rank runs this call:
+ *     *d_global_sqnorm   = ((slot_sqnorm[0] + slot_sqnorm[1]) + ...) + slot_sqnorm[n_ranks-1]
+ *     *d_global_overflow = 1 if any slot_overflow[r] != 0, else 0
+ * The sum is taken in rank order in fp64, so every rank obtains the same bits
+ * whatever order the slots arrived in.  Its outputs then feed
+ * zero_shard_adam_step (or zero_step_decide_dev and the update).
+ *  slot_sqnorm    device, [n_ranks] double, 8-byte aligned
+ *  slot_overflow  device, [n_ranks] int32, 4-byte aligned
+ *  n_ranks        1 <= n_ranks <= ZERO_MAX_RANKS
+ *  d_global_sqnorm, d_global_overflow  device outputs; nothing may overlap
+ * One one-workgroup kernel is enqueued.
+ * Errors: ZERO_EINVAL (bad n_ranks, NULL, overlap), ZERO_EALIGN, ZERO_EHIP.
+ * ------------------------------------------------------------------------- */
+#define ZERO_MAX_RANKS 65536
+int zero_norm_combine_ranks(const double* slot_sqnorm, const int32_t* slot_overflow, int32_t n_ranks,
+                            double* d_global_sqnorm, int32_t* d_global_overflow, void* hip_stream);
+
 /* Static description of a status code, and the thread-local detail of the
  * last failing call (empty string if none). */
 const char* zero_status_string(int status);

@@ -404,3 +404,21 @@ def test_scalar_and_workspace_aliasing_rejected_on_host():
     assert sn(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 8, al + 520, al + 1024, ws, None) == L.ZERO_EINVAL  # sq in acc
     assert sn(al, one, 1, L.ZERO_F16, 8, 0, 1.0, al + 512, al + 20, al + 1024, ws, None) == L.ZERO_EINVAL  # flag in acc
     assert "lies in" in lib.zero_last_error().decode()
+
+
+def test_norm_combine_rejects_bad_arguments_on_host():
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(4096)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    f = lib.zero_norm_combine_ranks
+    # slots: 8 doubles at al, 8 flags at al + 64; outputs at al + 512 / al + 520
+    assert f(al, al + 64, 0, al + 512, al + 520, None) == L.ZERO_EINVAL                   # no ranks
+    assert f(al, al + 64, 65537, al + 512, al + 520, None) == L.ZERO_EINVAL               # above the maximum
+    assert f(None, al + 64, 8, al + 512, al + 520, None) == L.ZERO_EINVAL
+    assert f(al, al + 64, 8, None, al + 520, None) == L.ZERO_EINVAL
+    assert f(al + 4, al + 64, 8, al + 512, al + 520, None) == L.ZERO_EALIGN
+    assert f(al, al + 66, 8, al + 512, al + 520, None) == L.ZERO_EALIGN
+    assert f(al, al + 32, 8, al + 512, al + 520, None) == L.ZERO_EINVAL                   # flags inside the sums
+    assert f(al, al + 64, 8, al + 8, al + 520, None) == L.ZERO_EINVAL                     # output inside a slot array
+    assert f(al, al + 64, 8, al + 512, al + 68, None) == L.ZERO_EINVAL
+    assert f(al, al + 64, 8, al + 512, al + 516, None) == L.ZERO_EINVAL                   # outputs overlap

@@ -315,6 +315,20 @@ class StepGraph:
             pass
 
 
+MAX_RANKS = 65536
+
+
+def zero_norm_combine_ranks(slot_sqnorm, slot_overflow, global_sqnorm, global_overflow, stream=None) -> None:
+    """The local half of the scalars' all-reduce: global_sqnorm = the rank-order
+    fp64 sum of slot_sqnorm (float64 [n_ranks]), global_overflow = the OR of
+    slot_overflow (int32 [n_ranks]); all device tensors."""
+    n = slot_sqnorm.numel()
+    if slot_overflow.numel() != n:
+        raise ValueError("slot_sqnorm and slot_overflow must have one entry per rank")
+    _L.check(_L.lib().zero_norm_combine_ranks(_ptr(slot_sqnorm), _ptr(slot_overflow), n, _ptr(global_sqnorm),
+                                              _ptr(global_overflow), _stream(stream)), "zero_norm_combine_ranks")
+
+
 def zero_copy_reference(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
     """Reference 16-byte-per-lane device copy of nbytes (default: all of src)."""
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
