@@ -109,6 +109,45 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_ELEM_BYTES = {ZERO_F16: 2, ZERO_BF16: 2, ZERO_F32: 4}
+
+
+def _dev(t, nbytes: int, what: str) -> Optional[int]:
+    """_ptr(t), after checking that the tensor holds the nbytes the call reads
+    or writes from its start, so that a short buffer raises here instead of
+    being overrun on the device.  A raw address is taken as it is."""
+    p = _ptr(t)
+    if t is not None and not isinstance(t, int):
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what}: {have} bytes, the call accesses {nbytes}")
+    return p
+
+
+def _typed(t, dtype_name: str, count: int, what: str) -> Optional[int]:
+    """Device pointer of a float64 / int32 scalar (or per-rank) buffer of at
+    least count elements."""
+    if t is None or isinstance(t, int):
+        return t
+    if str(t.dtype) != "torch." + dtype_name:
+        raise ValueError(f"{what}: torch.{dtype_name} tensor expected, got {t.dtype}")
+    return _dev(t, count * t.element_size(), what)
+
+
+def _grad_ptr(t, gd: int, n: int, what: str = "grad") -> Optional[int]:
+    return _dev(t, n * _ELEM_BYTES.get(gd, 0), what)
+
+
+def _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd: int, param_out, n: int):
+    """Checked pointers of the five shard streams of an update over n elements."""
+    return (_dev(master, 4 * n, "master"), _dev(exp_avg, 4 * n, "exp_avg"), _dev(exp_avg_sq, 4 * n, "exp_avg_sq"),
+            _grad_ptr(grad, gd, n), _dev(param_out, 2 * n, "param_out"))
+
+
+def _coef_ptr(d_coef) -> Optional[int]:
+    return _dev(d_coef, zero_adam_coef_bytes(), "d_coef")
+
+
 def zero_shard_unscale_norm_overflow(grad, inv_loss_scale: float, sqnorm, overflow, workspace,
                                      grad_dtype: Optional[int] = None, n: Optional[int] = None,
                                      stream=None) -> None:
@@ -119,8 +158,10 @@ def zero_shard_unscale_norm_overflow(grad, inv_loss_scale: float, sqnorm, overfl
     gd = dtype_code(grad if grad_dtype is None else grad_dtype)
     n = grad.numel() if n is None else n
     wbytes = workspace.numel() * workspace.element_size()
-    _L.check(_L.lib().zero_shard_unscale_norm_overflow(_ptr(grad), gd, n, float(inv_loss_scale), _ptr(sqnorm),
-                                                       _ptr(overflow), _ptr(workspace), wbytes, _stream(stream)),
+    _L.check(_L.lib().zero_shard_unscale_norm_overflow(_grad_ptr(grad, gd, n), gd, n, float(inv_loss_scale),
+                                                       _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                       _typed(overflow, "int32", 1, "overflow"), _ptr(workspace),
+                                                       wbytes, _stream(stream)),
              "zero_shard_unscale_norm_overflow")
 
 
@@ -151,9 +192,10 @@ def zero_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: AdamH
             if t.numel() != n:
                 raise ValueError("shard tensors differ in length")
     params = hp.c()
-    _L.check(_L.lib().zero_shard_adam_step(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
-                                           _ptr(param_out), pd, n, ctypes.byref(params), _ptr(global_sqnorm),
-                                           _ptr(global_overflow), _stream(stream)),
+    pm, pe, pv, pg, pp = _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd, param_out, n)
+    _L.check(_L.lib().zero_shard_adam_step(pm, pe, pv, pg, gd, pp, pd, n, ctypes.byref(params),
+                                           _typed(global_sqnorm, "float64", 1, "global_sqnorm"),
+                                           _typed(global_overflow, "int32", 1, "global_overflow"), _stream(stream)),
              "zero_shard_adam_step")
 
 
@@ -165,8 +207,9 @@ def zero_shard_grad_accumulate(acc, grad, inv_loss_scale: float, first: bool, ov
     n = acc.numel() if n is None else n
     if not isinstance(acc, int) and grad.numel() != n:
         raise ValueError("acc and grad differ in length")
-    _L.check(_L.lib().zero_shard_grad_accumulate(_ptr(acc), _ptr(grad), gd, n, float(inv_loss_scale),
-                                                 1 if first else 0, _ptr(overflow), _stream(stream)),
+    _L.check(_L.lib().zero_shard_grad_accumulate(_dev(acc, 4 * n, "acc"), _grad_ptr(grad, gd, n), gd, n,
+                                                 float(inv_loss_scale), 1 if first else 0,
+                                                 _typed(overflow, "int32", 1, "overflow"), _stream(stream)),
              "zero_shard_grad_accumulate")
 
 
@@ -184,9 +227,10 @@ def zero_shard_grad_reduce(acc, slices, inv_loss_scale: float, overflow=None, gr
         raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
     gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
     n = acc.numel() if n is None else n
-    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
-    _L.check(_L.lib().zero_shard_grad_reduce(_ptr(acc), arr, len(slices), gd, n, float(inv_loss_scale),
-                                             _ptr(overflow), _stream(stream)), "zero_shard_grad_reduce")
+    arr = (ctypes.c_void_p * len(slices))(*[_grad_ptr(t, gd, n, f"slices[{i}]") for i, t in enumerate(slices)])
+    _L.check(_L.lib().zero_shard_grad_reduce(_dev(acc, 4 * n, "acc"), arr, len(slices), gd, n,
+                                             float(inv_loss_scale), _typed(overflow, "int32", 1, "overflow"),
+                                             _stream(stream)), "zero_shard_grad_reduce")
 
 
 def _host_ptr(a) -> Optional[int]:
@@ -266,9 +310,11 @@ def zero_shard_adam_step_coef(master, exp_avg, exp_avg_sq, grad, param_out, d_co
     gd = dtype_code(grad if grad_dtype is None else grad_dtype)
     pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
     n = master.numel() if n is None else n
-    _L.check(_L.lib().zero_shard_adam_step_coef(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
-                                                _ptr(param_out), pd, n, _ptr(d_coef), _ptr(global_sqnorm),
-                                                _ptr(global_overflow), _stream(stream)),
+    pm, pe, pv, pg, pp = _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd, param_out, n)
+    _L.check(_L.lib().zero_shard_adam_step_coef(pm, pe, pv, pg, gd, pp, pd, n, _coef_ptr(d_coef),
+                                                _typed(global_sqnorm, "float64", 1, "global_sqnorm"),
+                                                _typed(global_overflow, "int32", 1, "global_overflow"),
+                                                _stream(stream)),
              "zero_shard_adam_step_coef")
 
 
@@ -284,10 +330,11 @@ class StepGraph:
         pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
         handle = ctypes.c_void_p()
         wbytes = workspace.numel() * workspace.element_size()
-        _L.check(_L.lib().zero_step_graph_create(ctypes.byref(handle), _ptr(master), _ptr(exp_avg),
-                                                 _ptr(exp_avg_sq), _ptr(grad), gd, _ptr(param_out), pd,
-                                                 master.numel(), float(inv_loss_scale), _ptr(sqnorm),
-                                                 _ptr(overflow), _ptr(workspace), wbytes),
+        n = master.numel()
+        pm, pe, pv, pg, pp = _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd, param_out, n)
+        _L.check(_L.lib().zero_step_graph_create(ctypes.byref(handle), pm, pe, pv, pg, gd, pp, pd, n,
+                                                 float(inv_loss_scale), _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                 _typed(overflow, "int32", 1, "overflow"), _ptr(workspace), wbytes),
                  "zero_step_graph_create")
         self._h = handle.value
         self.inv_loss_scale = float(inv_loss_scale)
@@ -325,14 +372,18 @@ def zero_norm_combine_ranks(slot_sqnorm, slot_overflow, global_sqnorm, global_ov
     n = slot_sqnorm.numel()
     if slot_overflow.numel() != n:
         raise ValueError("slot_sqnorm and slot_overflow must have one entry per rank")
-    _L.check(_L.lib().zero_norm_combine_ranks(_ptr(slot_sqnorm), _ptr(slot_overflow), n, _ptr(global_sqnorm),
-                                              _ptr(global_overflow), _stream(stream)), "zero_norm_combine_ranks")
+    _L.check(_L.lib().zero_norm_combine_ranks(_typed(slot_sqnorm, "float64", n, "slot_sqnorm"),
+                                              _typed(slot_overflow, "int32", n, "slot_overflow"), n,
+                                              _typed(global_sqnorm, "float64", 1, "global_sqnorm"),
+                                              _typed(global_overflow, "int32", 1, "global_overflow"),
+                                              _stream(stream)), "zero_norm_combine_ranks")
 
 
 def zero_copy_reference(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
     """Reference 16-byte-per-lane device copy of nbytes (default: all of src)."""
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
-    _L.check(_L.lib().zero_copy_reference(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)), "zero_copy_reference")
+    _L.check(_L.lib().zero_copy_reference(_dev(dst, int(nbytes), "dst"), _dev(src, int(nbytes), "src"), int(nbytes),
+                                          _stream(stream)), "zero_copy_reference")
 
 
 class StepState:
@@ -364,8 +415,9 @@ def zero_shard_unscale_norm_overflow_dev(grad, state: StepState, sqnorm, overflo
                                          stream=None) -> None:
     gd = dtype_code(grad if grad_dtype is None else grad_dtype)
     n = grad.numel() if n is None else n
-    _L.check(_L.lib().zero_shard_unscale_norm_overflow_dev(_ptr(grad), gd, n, state.ptr(), _ptr(sqnorm),
-                                                           _ptr(overflow), _ptr(workspace),
+    _L.check(_L.lib().zero_shard_unscale_norm_overflow_dev(_grad_ptr(grad, gd, n), gd, n, state.ptr(),
+                                                           _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                           _typed(overflow, "int32", 1, "overflow"), _ptr(workspace),
                                                            workspace.numel() * workspace.element_size(),
                                                            _stream(stream)), "zero_shard_unscale_norm_overflow_dev")
 
@@ -378,10 +430,11 @@ def zero_shard_adam_step_dev(master, exp_avg, exp_avg_sq, grad, param_out, hp: "
     pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
     n = master.numel() if n is None else n
     h = _hyper(hp)
-    _L.check(_L.lib().zero_shard_adam_step_dev(_ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), gd,
-                                               _ptr(param_out), pd, n, ctypes.byref(h), state.ptr(),
-                                               _ptr(global_sqnorm), _ptr(global_overflow), _ptr(d_coef),
-                                               _stream(stream)), "zero_shard_adam_step_dev")
+    pm, pe, pv, pg, pp = _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd, param_out, n)
+    _L.check(_L.lib().zero_shard_adam_step_dev(pm, pe, pv, pg, gd, pp, pd, n, ctypes.byref(h), state.ptr(),
+                                               _typed(global_sqnorm, "float64", 1, "global_sqnorm"),
+                                               _typed(global_overflow, "int32", 1, "global_overflow"),
+                                               _coef_ptr(d_coef), _stream(stream)), "zero_shard_adam_step_dev")
 
 
 def zero_shard_norm_decide_dev(grad, hp: "AdamHyper", state: StepState, sqnorm, overflow, d_coef, workspace,
@@ -390,8 +443,10 @@ def zero_shard_norm_decide_dev(grad, hp: "AdamHyper", state: StepState, sqnorm, 
     gd = dtype_code(grad if grad_dtype is None else grad_dtype)
     n = grad.numel() if n is None else n
     h = _hyper(hp)
-    _L.check(_L.lib().zero_shard_norm_decide_dev(_ptr(grad), gd, n, ctypes.byref(h), state.ptr(), _ptr(sqnorm),
-                                                 _ptr(overflow), _ptr(d_coef), _ptr(workspace),
+    _L.check(_L.lib().zero_shard_norm_decide_dev(_grad_ptr(grad, gd, n), gd, n, ctypes.byref(h), state.ptr(),
+                                                 _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                 _typed(overflow, "int32", 1, "overflow"), _coef_ptr(d_coef),
+                                                 _ptr(workspace),
                                                  workspace.numel() * workspace.element_size(), _stream(stream)),
              "zero_shard_norm_decide_dev")
 
@@ -401,7 +456,8 @@ def zero_step_decide_dev(hp: "AdamHyper", grad_dtype, state: StepState, global_o
     """The decision kernel: d_coef <- coefficients of step applied+1, state advanced by the flag."""
     h = _hyper(hp)
     _L.check(_L.lib().zero_step_decide_dev(ctypes.byref(h), dtype_code(grad_dtype), state.ptr(),
-                                           _ptr(global_overflow), _ptr(d_coef), _stream(stream)),
+                                           _typed(global_overflow, "int32", 1, "global_overflow"),
+                                           _coef_ptr(d_coef), _stream(stream)),
              "zero_step_decide_dev")
 
 
@@ -409,8 +465,10 @@ def zero_shard_grad_accumulate_dev(acc, grad, state: StepState, first: bool, ove
                                    grad_dtype: Optional[int] = None, n: Optional[int] = None, stream=None) -> None:
     gd = dtype_code(grad if grad_dtype is None else grad_dtype)
     n = acc.numel() if n is None else n
-    _L.check(_L.lib().zero_shard_grad_accumulate_dev(_ptr(acc), _ptr(grad), gd, n, state.ptr(), 1 if first else 0,
-                                                     _ptr(overflow), _stream(stream)), "zero_shard_grad_accumulate_dev")
+    _L.check(_L.lib().zero_shard_grad_accumulate_dev(_dev(acc, 4 * n, "acc"), _grad_ptr(grad, gd, n), gd, n,
+                                                     state.ptr(), 1 if first else 0,
+                                                     _typed(overflow, "int32", 1, "overflow"), _stream(stream)),
+             "zero_shard_grad_accumulate_dev")
 
 
 def zero_shard_grad_reduce_dev(acc, slices, state: StepState, overflow=None, grad_dtype: Optional[int] = None,
@@ -419,9 +477,10 @@ def zero_shard_grad_reduce_dev(acc, slices, state: StepState, overflow=None, gra
         raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
     gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
     n = acc.numel() if n is None else n
-    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
-    _L.check(_L.lib().zero_shard_grad_reduce_dev(_ptr(acc), arr, len(slices), gd, n, state.ptr(), _ptr(overflow),
-                                                 _stream(stream)), "zero_shard_grad_reduce_dev")
+    arr = (ctypes.c_void_p * len(slices))(*[_grad_ptr(t, gd, n, f"slices[{i}]") for i, t in enumerate(slices)])
+    _L.check(_L.lib().zero_shard_grad_reduce_dev(_dev(acc, 4 * n, "acc"), arr, len(slices), gd, n, state.ptr(),
+                                                 _typed(overflow, "int32", 1, "overflow"), _stream(stream)),
+             "zero_shard_grad_reduce_dev")
 
 
 def zero_sum_norm_workspace_bytes(n: int) -> int:
@@ -436,9 +495,11 @@ def zero_shard_grad_sum_norm(acc, slices, add_to_acc: bool, inv_loss_scale: floa
         raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
     gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
     n = acc.numel() if n is None else n
-    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
-    _L.check(_L.lib().zero_shard_grad_sum_norm(_ptr(acc), arr, len(slices), gd, n, 1 if add_to_acc else 0,
-                                               float(inv_loss_scale), _ptr(sqnorm), _ptr(overflow), _ptr(workspace),
+    arr = (ctypes.c_void_p * len(slices))(*[_grad_ptr(t, gd, n, f"slices[{i}]") for i, t in enumerate(slices)])
+    _L.check(_L.lib().zero_shard_grad_sum_norm(_dev(acc, 4 * n, "acc"), arr, len(slices), gd, n,
+                                               1 if add_to_acc else 0, float(inv_loss_scale),
+                                               _typed(sqnorm, "float64", 1, "sqnorm"),
+                                               _typed(overflow, "int32", 1, "overflow"), _ptr(workspace),
                                                workspace.numel() * workspace.element_size(), _stream(stream)),
              "zero_shard_grad_sum_norm")
 
@@ -452,10 +513,13 @@ def zero_shard_grad_sum_norm_dev(acc, slices, add_to_acc: bool, state: StepState
         raise ValueError(f"1 to {MAX_SLICES} slices expected, got {len(slices)}")
     gd = dtype_code(slices[0] if grad_dtype is None else grad_dtype)
     n = acc.numel() if n is None else n
-    arr = (ctypes.c_void_p * len(slices))(*[_ptr(t) for t in slices])
+    arr = (ctypes.c_void_p * len(slices))(*[_grad_ptr(t, gd, n, f"slices[{i}]") for i, t in enumerate(slices)])
     h = None if hp is None else ctypes.byref(_hyper(hp))
-    _L.check(_L.lib().zero_shard_grad_sum_norm_dev(_ptr(acc), arr, len(slices), gd, n, 1 if add_to_acc else 0, h,
-                                                   state.ptr(), _ptr(sqnorm), _ptr(overflow), _ptr(d_coef),
+    _L.check(_L.lib().zero_shard_grad_sum_norm_dev(_dev(acc, 4 * n, "acc"), arr, len(slices), gd, n,
+                                                   1 if add_to_acc else 0, h, state.ptr(),
+                                                   _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                   _typed(overflow, "int32", 1, "overflow"),
+                                                   None if d_coef is None else _coef_ptr(d_coef),
                                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                                    _stream(stream)), "zero_shard_grad_sum_norm_dev")
 
@@ -472,10 +536,13 @@ class StepGraphDev:
         pd = 0 if param_out is None else dtype_code(param_out if param_dtype is None else param_dtype)
         handle = ctypes.c_void_p()
         h = _hyper(hp)
-        _L.check(_L.lib().zero_step_graph_create_dev(ctypes.byref(handle), _ptr(master), _ptr(exp_avg),
-                                                     _ptr(exp_avg_sq), _ptr(grad), gd, _ptr(param_out), pd,
-                                                     master.numel(), ctypes.byref(h), state.ptr(), _ptr(sqnorm),
-                                                     _ptr(overflow), _ptr(d_coef), _ptr(workspace),
+        n = master.numel()
+        pm, pe, pv, pg, pp = _step_ptrs(master, exp_avg, exp_avg_sq, grad, gd, param_out, n)
+        _L.check(_L.lib().zero_step_graph_create_dev(ctypes.byref(handle), pm, pe, pv, pg, gd, pp, pd, n,
+                                                     ctypes.byref(h), state.ptr(),
+                                                     _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                     _typed(overflow, "int32", 1, "overflow"), _coef_ptr(d_coef),
+                                                     _ptr(workspace),
                                                      workspace.numel() * workspace.element_size()),
                  "zero_step_graph_create_dev")
         self._h = handle.value
