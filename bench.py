@@ -421,13 +421,14 @@ def main():
                        "avg_ms": acc_ms,
                        "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
                        "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
-                       "traffic": measured_traffic(run_key, "grad_accumulate")}
+                       "traffic": measured_traffic(run_key, "grad_sum_norm" if FUSED else "grad_accumulate")}
     reduce_stats = None
     if R:
         red_ms = mean([e[3].elapsed_time(e[4]) for e in evs])
         reduce_stats = {"slices": R, "kernel": "grad_sum_norm (with the norm)" if FUSED else "grad_reduce",
                         "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
-                        "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9, "traffic": measured_traffic(run_key, "grad_reduce")}
+                        "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9,
+                        "traffic": measured_traffic(run_key, "grad_sum_norm" if FUSED else "grad_reduce")}
 
     # the achievable rate of one read + one write stream over the same 14 B/param
     # each way (at most 16 GiB): the library's reference copy kernel, and

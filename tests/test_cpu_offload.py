@@ -127,3 +127,30 @@ def test_worker_pool_survives_fork():
     _, status = os.waitpid(pid, 0)
     assert os.WIFEXITED(status) and os.WEXITSTATUS(status) == 0
     assert Z.zero_cpu_shard_unscale_norm_overflow(g, 2.0) == (4.0 * (1 << 20), False)
+
+
+@pytest.mark.parametrize("gfmt", ["bf16", "f32"])
+def test_cpu_step_huge_unclipped_gradients(gfmt):
+    """Gradients whose square passes float32's range (|g| up to 4e20, no
+    clipping) while (1 - beta2) g^2 does not: the second moment stays finite
+    and the step matches the oracle."""
+    n = 20_011
+    w = W.LLAMA_7B
+    p, m, v, _ = W.shard_inputs(w, 777, n)
+    rng = np.random.default_rng(99)
+    x = rng.normal(0.0, 1e-3, n)
+    k = np.arange(0, n, 7)
+    x[k] = np.sign(rng.normal(size=k.size)) * 10.0 ** rng.uniform(19.0, np.log10(4e20), k.size)
+    g = x.astype(np.float32) if gfmt == "f32" else oracle.encode16_rne(x.astype(np.float32), "bf16")
+    sq, ovf = Z.zero_cpu_shard_unscale_norm_overflow(g, 1.0, grad_dtype=CODE[gfmt])
+    ref_sq, _ = oracle.shard_sqnorm_overflow(g, gfmt, 1.0)
+    check_norm(sq, ref_sq)
+    P, M, V = p.copy(), m.copy(), v.copy()
+    par = np.zeros(n, np.uint16)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.01, max_grad_norm=0.0,
+              step=5, inv_loss_scale=1.0)
+    Z.zero_cpu_shard_adam_step(P, M, V, g, par, Z.AdamHyper(**hp), sq, ovf, grad_dtype=CODE[gfmt],
+                               param_dtype=L.ZERO_BF16)
+    ref = oracle.shard_step(p, m, v, g, gfmt, "bf16", global_sq=ref_sq, global_overflow=False, **hp)
+    assert np.isfinite(V).all()
+    compare_step((P, M, V, par), ref)

@@ -161,7 +161,7 @@ ZS_CLONES void adam_f32(float* __restrict p, float* __restrict m, float* __restr
     for (int i = 0; i < n; ++i) {
         const float gi = g[i] * gscale;
         const float mi = b1 * m[i] + omb1 * gi;
-        const float vi = b2 * v[i] + omb2 * (gi * gi);
+        const float vi = b2 * v[i] + (omb2 * gi) * gi;      // finite wherever v is (g g alone overflows past 2^64)
         const float denom = std::sqrt(vi) * rsqrt_bc2 + eps;
         p[i] = p[i] * decay - (step_size * mi) / denom;
         m[i] = mi;

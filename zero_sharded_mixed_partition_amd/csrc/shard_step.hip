@@ -386,7 +386,10 @@ __device__ __forceinline__ void adam_elem(const StepCoef& c, float gscale, float
                                           float& v) {
     const float g = graw * gscale;
     m = fmaf(c.beta1, m, c.omb1 * g);
-    v = fmaf(c.beta2, v, c.omb2 * (g * g));
+    // (1 - beta2) g^2 as ((1 - beta2) g) g: the same three roundings as
+    // (1 - beta2)(g g), but finite wherever the stored moment is, where g g
+    // alone would overflow float32 once |g| passes 2^64
+    v = fmaf(c.beta2, v, (c.omb2 * g) * g);
     const float denom = fmaf(sqrtf(v), c.rsqrt_bc2, c.eps);
     p = fmaf(p, c.decay, -(c.step_size * m) / denom);
 }
