@@ -88,6 +88,12 @@ constexpr int kEwTask = 4 * kEwThreads;                         // elements per 
 // 4 per CU 73-75%; 2 tasks ~79%.  Four tasks would make a skipped step 4x
 // cheaper (every workgroup reads the flag and exits: 0.2 instead of 0.8 ms on
 // that shard), but skipped steps are rare and applied ones are not.
+// Task t goes to workgroup t, so consecutive 1 KiB runs of each stream go to
+// the 8 XCDs in turn and the chip streams one narrow window of every buffer.
+// Measured over several processes each on the 976M-element shard: XCDs
+// streaming their own contiguous eighths ~76%, 2 or 4 consecutive tasks per
+// XCD ~80.5% / ~78%, and 512 B tasks (2 elements per lane) ~75-76%, against
+// ~81.7% for this layout.
 constexpr size_t kAdamLdsReserve = 12 * 1024;
 constexpr int kAdamTasks = 1;
 constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per workgroup
