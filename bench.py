@@ -16,6 +16,7 @@ reports the fused AdamW kernel (the dominant one) against MI355X's 8 TB/s HBM
 peak, from HIP events recorded on the stream it runs on.
 """
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -246,6 +247,9 @@ def main():
                     help="keep the loss scaler and step counter on the host, reading the 4-byte overflow flag back "
                          "every step (default: both live in device memory and no step waits for the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--alloc", choices=["contiguous", "torch"], default="contiguous",
+                    help="where the shard's buffers come from: physically contiguous HBM through the library's "
+                         "allocator in a torch memory pool (default), or torch's default allocator")
     args = ap.parse_args()
     if args.graph and (args.accum or args.offload or args.reduce):
         print("--graph records the 16-bit-gradient step on the GPU; it does not combine with --accum, "
@@ -282,9 +286,18 @@ def main():
     offsets, S, padded = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
     begin = w.rank * S
     print(f"# workload {w.name}: shard {S} params at flat offset {begin}", file=sys.stderr, flush=True)
-    P, M, V, G = upload_inputs(w, begin, S, w.grad_dtype)
-    pdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.param_dtype]
-    par = torch.empty(S, dtype=pdt, device="cuda")
+    # the shard's streams: physically contiguous HBM by default (the update
+    # kernel's rate depends on where its eight streams' pages land)
+    pool_ctx = torch.cuda.use_mem_pool(Z.contiguous_pool()) if args.alloc == "contiguous" else contextlib.nullcontext()
+    K = args.accum
+    R = args.reduce
+    with pool_ctx:
+        P, M, V, G = upload_inputs(w, begin, S, w.grad_dtype)
+        pdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.param_dtype]
+        par = torch.empty(S, dtype=pdt, device="cuda")
+        A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
+        # the other ranks' slices: copies of this rank's gradient (distinct buffers, same values)
+        slices = [G] + [G.clone() for _ in range(R - 1)] if R else None
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
@@ -292,11 +305,6 @@ def main():
                       device_state=not args.host_scaler)
     DS = opt.state is not None
     FUSED = bool(args.accum or args.reduce) and not args.separate_norm
-    K = args.accum
-    R = args.reduce
-    A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
-    # the other ranks' slices: copies of this rank's gradient (distinct buffers, same values)
-    slices = [G] + [G.clone() for _ in range(R - 1)] if R else None
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -475,7 +483,9 @@ def main():
                    + ((", norm in the pass that writes the copy" if FUSED else ", separate norm pass") if (K or R) else "")
                    + (", recorded step graph" if args.graph else "")
                    + (", scaler and step counter in device memory" if DS else ", host loss scaler (4-byte flag read per step)"),
-                   "algorithmic_bytes_per_param": step_bpp},
+                   "algorithmic_bytes_per_param": step_bpp,
+                   "buffers": ("physically contiguous HBM (library allocator behind a torch memory pool)"
+                               if args.alloc == "contiguous" else "torch default allocator")},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "kernel": "adam_update_devcoef" if DS else "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,

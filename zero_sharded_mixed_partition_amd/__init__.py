@@ -34,7 +34,8 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
            "zero_shard_norm_decide_dev", "StepGraphDev", "zero_sum_norm_workspace_bytes", "zero_shard_grad_sum_norm",
-           "zero_shard_grad_sum_norm_dev"]
+           "zero_shard_grad_sum_norm_dev", "zero_device_alloc_contiguous", "zero_device_free",
+           "contiguous_pool"]
 
 
 def zero_abi_version() -> int:
@@ -594,3 +595,42 @@ def zero_loss_scaler_update(scaler: LossScaler, overflow: bool) -> bool:
 from .shard import ShardAdam  # noqa: E402
 from .offload import OffloadShardAdam  # noqa: E402
 from . import checkpoint  # noqa: E402,F401
+
+
+# ---------------------------------------------------------------- physically contiguous HBM
+
+def zero_device_alloc_contiguous(nbytes: int) -> int:
+    """Address of `nbytes` of physically contiguous device memory (0 for 0
+    bytes); release it with zero_device_free."""
+    p = ctypes.c_void_p()
+    _L.check(_L.lib().zero_device_alloc_contiguous(ctypes.byref(p), int(nbytes)), "zero_device_alloc_contiguous")
+    return p.value or 0
+
+
+def zero_device_free(ptr: int) -> None:
+    _L.check(_L.lib().zero_device_free(ptr or None), "zero_device_free")
+
+
+_POOLS = {}
+
+
+def contiguous_pool(device=None):
+    """A torch memory pool whose segments are physically contiguous device
+    memory (zero_pool_alloc / zero_pool_free).  Allocate a shard's buffers
+    inside it:
+
+        with torch.cuda.use_mem_pool(Z.contiguous_pool()):
+            master = torch.empty(S, dtype=torch.float32, device="cuda")
+
+    Freed tensors return to the pool; the pool (one per device, kept for the
+    life of the process) must outlive them."""
+    import torch
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    if dev is None:
+        dev = torch.cuda.current_device()
+    if dev not in _POOLS:
+        _L.lib()                                   # fails loudly if the library is missing
+        alloc = torch.cuda.memory.CUDAPluggableAllocator(_L.LIB_PATH, "zero_pool_alloc", "zero_pool_free")
+        with torch.cuda.device(dev):
+            _POOLS[dev] = (alloc, torch.cuda.MemPool(alloc.allocator()))
+    return _POOLS[dev][1]

@@ -77,6 +77,10 @@ SIGNATURES = {
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
     "zero_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
+    "zero_device_alloc_contiguous": (c_i32, [ctypes.POINTER(c_vp), c_sz]),
+    "zero_device_free": (c_i32, [c_vp]),
+    "zero_pool_alloc": (c_vp, [c_sz, c_i32, c_vp]),
+    "zero_pool_free": (None, [c_vp, c_sz, c_i32, c_vp]),
     "zero_norm_combine_ranks": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "zero_shard_unscale_norm_overflow_dev": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "zero_shard_norm_decide_dev": (c_i32, [c_vp, c_i32, c_i64, ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp,

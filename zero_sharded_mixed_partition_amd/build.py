@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libzero_shard.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 HOST_SOURCES = ["host.cpp", "cpu_step.cpp"]      # host C++ only (built by the host compiler)
-DEVICE_SOURCES = ["shard_step.hip", "combine.hip", "copy_ref.hip"]   # HIP: host launchers + gfx950 kernels
+DEVICE_SOURCES = ["shard_step.hip", "combine.hip", "copy_ref.hip", "hbm_alloc.hip"]   # HIP: host launchers + gfx950 kernels
 SOURCES = HOST_SOURCES + DEVICE_SOURCES
 ARCH = "gfx950"
 
