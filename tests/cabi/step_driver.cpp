@@ -77,6 +77,25 @@ void free_shard(Shard& s) {
     (void)hipFree(s.PO);
 }
 
+// the same five streams from the library's physically contiguous memory
+int alloc_shard_contiguous(Shard& s, int64_t n) {
+    int st = zero_device_alloc_contiguous((void**)&s.P, n * 4);
+    if (st == ZERO_OK) st = zero_device_alloc_contiguous((void**)&s.M, n * 4);
+    if (st == ZERO_OK) st = zero_device_alloc_contiguous((void**)&s.V, n * 4);
+    if (st == ZERO_OK) st = zero_device_alloc_contiguous((void**)&s.G, n * 2);
+    if (st == ZERO_OK) st = zero_device_alloc_contiguous((void**)&s.PO, n * 2);
+    CHECK(st == ZERO_OK, "contiguous allocation: %s", zero_last_error());
+    return 0;
+}
+
+void free_shard_contiguous(Shard& s) {
+    (void)zero_device_free(s.P);
+    (void)zero_device_free(s.M);
+    (void)zero_device_free(s.V);
+    (void)zero_device_free(s.G);
+    (void)zero_device_free(s.PO);
+}
+
 }  // namespace
 
 int main() {
@@ -163,7 +182,7 @@ int main() {
 
     // the same first step with the loss scaler and step counter in device memory
     Shard b;
-    if (alloc_shard(b, n)) return 1;
+    if (alloc_shard_contiguous(b, n)) return 1;        // this one from physically contiguous memory
     HIP_OK(hipMemcpy(b.P, p0.data(), n * 4, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(b.M, zeros.data(), n * 4, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(b.V, zeros.data(), n * 4, hipMemcpyHostToDevice));
@@ -202,7 +221,7 @@ int main() {
     CHECK(zero_last_error()[0] != '\0' && zero_status_string(st) != nullptr, "no error detail");
 
     free_shard(a);
-    free_shard(b);
+    free_shard_contiguous(b);
     (void)hipFree(d_sq);
     (void)hipFree(d_ovf);
     (void)hipFree(d_ws);
