@@ -115,27 +115,65 @@ def shard_sqnorm_overflow(grad_bits: np.ndarray, fmt: str, inv_loss_scale: float
     return float(exact), False
 
 
+@dataclass(frozen=True)
+class SqnormTerms:
+    """What one shard contributes to the global (sum of squares, flag), in a
+    form whose contributions add up without rounding: for a 16-bit gradient
+    the histogram of its finite magnitudes (counts per pattern, sign dropped);
+    for an fp32 gradient the float64 sums of its 2^24-element chunks of
+    (g * inv_loss_scale)^2.  overflow / has_nan: the shard holds an inf or
+    NaN / a NaN."""
+    counts: Optional[np.ndarray]
+    chunk_sums: Tuple[float, ...]
+    overflow: bool
+    has_nan: bool
+
+
+def sqnorm_terms(grad, fmt: str, inv_loss_scale: float) -> SqnormTerms:
+    """One shard's terms of the data-parallel norm reduction (see SqnormTerms)."""
+    if fmt == "f32":
+        x = np.asarray(grad, dtype=np.float32)
+        if not np.isfinite(x).all():
+            return SqnormTerms(None, (), True, bool(np.isnan(x).any()))
+        sums = []
+        for s in range(0, x.size, 1 << 24):
+            y = x[s:s + (1 << 24)].astype(np.float64) * inv_loss_scale
+            sums.append(float(np.sum(y * y)))
+        return SqnormTerms(None, tuple(sums), False, False)
+    bits = np.asarray(grad)
+    bad = is_nonfinite16(bits, fmt)
+    if bad.any():
+        return SqnormTerms(None, (), True, bool(np.isnan(decode16(bits[bad], fmt)).any()))
+    return SqnormTerms(_magnitude_counts(bits, fmt), (), False, False)
+
+
+def combine_sqnorm_terms(terms: Iterable[SqnormTerms], fmt: str, inv_loss_scale: float) -> Tuple[float, bool]:
+    """The data-parallel reduction: the OR of the shards' flags, and the sum
+    of squares over all shards, +inf if some shard holds an inf and none a
+    NaN, NaN if any holds a NaN.  16-bit: the histograms are added and the
+    sum formed exactly from them, rounded once.  fp32: math.fsum over every
+    shard's chunk sums (each chunk summed pairwise in float64, so the result
+    is within 1e-14 relative of the exact sum)."""
+    counts, sums, overflow, has_nan = np.zeros(0x8000, np.int64), [], False, False
+    for t in terms:
+        overflow |= t.overflow
+        has_nan |= t.has_nan
+        if t.counts is not None:
+            counts += t.counts
+        sums.extend(t.chunk_sums)
+    if overflow:
+        return (math.nan if has_nan else math.inf), True
+    if fmt == "f32":
+        return math.fsum(sums), False
+    return float(_sum_squares_from_counts(counts, fmt) * Fraction(inv_loss_scale) ** 2), False
+
+
 def global_sqnorm_overflow(shards: Iterable[np.ndarray], fmt: str,
                            inv_loss_scale: float) -> Tuple[float, bool]:
     """The data-parallel reduction of the per-rank results: the global sum of
-    squares over all shards (exact, one rounding) and the OR of the flags."""
-    if fmt == "f32":
-        parts = [_sqnorm_overflow_f32(g, inv_loss_scale) for g in shards]
-        if any(o for _, o in parts):
-            return (math.nan if any(math.isnan(q) for q, _ in parts) else math.inf), True
-        return math.fsum(q for q, _ in parts), False
-    counts, overflow, has_nan = np.zeros(0x8000, np.int64), False, False
-    for bits in shards:
-        bits = np.asarray(bits)
-        bad = is_nonfinite16(bits, fmt)
-        if bad.any():
-            overflow = True
-            has_nan |= bool(np.isnan(decode16(bits[bad], fmt)).any())
-        else:
-            counts += _magnitude_counts(bits, fmt)
-    if overflow:
-        return (math.nan if has_nan else math.inf), True
-    return float(_sum_squares_from_counts(counts, fmt) * Fraction(inv_loss_scale) ** 2), False
+    squares over all shards (16-bit: exact, one rounding) and the OR of the
+    flags."""
+    return combine_sqnorm_terms((sqnorm_terms(g, fmt, inv_loss_scale) for g in shards), fmt, inv_loss_scale)
 
 
 def clip_coefficient(sq: float, max_grad_norm: float) -> float:

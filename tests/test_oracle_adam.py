@@ -110,6 +110,82 @@ def test_global_equals_whole():
     assert global_sqnorm_overflow(shards, "f16", 2.0**-10) == shard_sqnorm_overflow(whole, "f16", 2.0**-10)
 
 
+_NAN16 = {"f16": 0x7E00, "bf16": 0x7FC0}
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_global_nonfinite_is_or_over_shards(fmt):
+    """The data-parallel OR: one non-finite element in any one of several
+    finite shards raises the global flag; the global sum is +inf when the
+    shards hold an infinity (of either sign) and no NaN, NaN as soon as any
+    shard holds a NaN, whichever shard comes first (IEEE: inf + x = inf,
+    NaN + x = NaN)."""
+    rng = np.random.default_rng(21)
+    shards = [_rand_bits(rng, 997 + 13 * k, fmt, 1e-3) for k in range(5)]
+    inf, nan = W.POS_INF_BITS[fmt], _NAN16[fmt]
+    assert global_sqnorm_overflow(shards, fmt, 1.0)[1] is False
+    for k in range(5):
+        for bits, want in ((inf, math.inf), (inf | 0x8000, math.inf)):
+            s = [a.copy() for a in shards]
+            s[k][k * 7] = bits
+            assert global_sqnorm_overflow(s, fmt, 1.0) == (want, True)
+        s = [a.copy() for a in shards]
+        s[k][-1] = nan
+        sq, ovf = global_sqnorm_overflow(s, fmt, 0.5)
+        assert ovf is True and math.isnan(sq)
+    for i, j in ((0, 4), (4, 0), (2, 2)):            # a NaN with an inf: NaN
+        s = [a.copy() for a in shards]
+        s[i][3] = nan
+        s[j][5] = inf
+        sq, ovf = global_sqnorm_overflow(s, fmt, 1.0)
+        assert ovf is True and math.isnan(sq)
+    # a NaN-free shard list whose finite part is empty: still +inf
+    assert global_sqnorm_overflow([np.array([inf], np.uint16), np.zeros(0, np.uint16)], fmt, 1.0) == \
+        (math.inf, True)
+
+
+def test_global_f32_shards_match_exact_sum():
+    """fp32 gradient shards (the accumulated copy): every square of an fp32
+    value times a power of two is exact in float64, so math.fsum over the
+    concatenated squares is the correctly rounded global sum; the oracle's
+    chunked sum lies within 1e-14 of it for any split into shards (it is
+    documented to), and equals it exactly where the partial sums are all
+    representable (equal powers of two)."""
+    rng = np.random.default_rng(23)
+    whole = (rng.standard_normal(300_007) * np.exp(rng.uniform(-8, 8, 300_007))).astype(np.float32)
+    for inv in (1.0, 2.0**-16, 0.5):
+        exact = math.fsum(((whole.astype(np.float64) * inv) ** 2).tolist())
+        for cuts in ((), (1,), (150_000,), (5, 77_777, 200_000, 300_006)):
+            shards = np.split(whole, list(cuts))
+            sq, ovf = global_sqnorm_overflow(shards, "f32", inv)
+            assert ovf is False and abs(sq - exact) <= 1e-14 * exact
+    # n copies of 2^-k, split unevenly: exactly n * 2^-2k
+    c = np.full(100_003, 2.0**-9, np.float32)
+    assert global_sqnorm_overflow(np.split(c, [3, 60_000]), "f32", 0.25) == (100_003 * 2.0**-18 / 16, False)
+    assert global_sqnorm_overflow([np.zeros(0, np.float32)], "f32", 1.0) == (0.0, False)
+
+
+def test_global_f32_nonfinite_is_or_over_shards():
+    rng = np.random.default_rng(25)
+    shards = [rng.standard_normal(1000 + k).astype(np.float32) for k in range(4)]
+    for k in range(4):
+        for bad, want in ((np.inf, math.inf), (-np.inf, math.inf)):
+            s = [a.copy() for a in shards]
+            s[k][k] = bad
+            assert global_sqnorm_overflow(s, "f32", 1.0) == (want, True)
+        s = [a.copy() for a in shards]
+        s[k][-1] = np.nan
+        sq, ovf = global_sqnorm_overflow(s, "f32", 1.0)
+        assert ovf is True and math.isnan(sq)
+    s = [a.copy() for a in shards]
+    s[0][0], s[3][0] = np.inf, np.nan
+    sq, ovf = global_sqnorm_overflow(s, "f32", 1.0)
+    assert ovf is True and math.isnan(sq)
+    # a finite fp32 value whose square overflows float32 is not an overflow
+    sq, ovf = shard_sqnorm_overflow(np.array([3e38, -3e38], np.float32), "f32", 1.0)
+    assert ovf is False and sq == 2 * float(np.float32(3e38)) ** 2
+
+
 # ---------------------------------------------------------------- clipping
 
 def test_clip_matches_torch():
