@@ -25,8 +25,9 @@ def _fields(fmt):
     return ebits, mbits, bias, emax_field, emin, emax
 
 
-def decode16(bits: np.ndarray, fmt: str) -> np.ndarray:
-    """Exact float64 value of each 16-bit pattern."""
+def _decode16_fields(bits: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact float64 value of each 16-bit pattern, from its sign, exponent and
+    fraction fields."""
     ebits, mbits, bias, emax_field, emin, _ = _fields(fmt)
     b = np.asarray(bits).astype(np.int64) & 0xFFFF
     sign = np.where(b >> 15, -1.0, 1.0)
@@ -41,6 +42,17 @@ def decode16(bits: np.ndarray, fmt: str) -> np.ndarray:
     return sign * val
 
 
+_DECODE_TABLE = {}
+
+
+def decode16(bits: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact float64 value of each 16-bit pattern: the field decoding above,
+    evaluated once for all 65,536 patterns and then looked up by pattern."""
+    if fmt not in _DECODE_TABLE:
+        _DECODE_TABLE[fmt] = _decode16_fields(np.arange(1 << 16, dtype=np.int64), fmt)
+    return _DECODE_TABLE[fmt][np.asarray(bits).astype(np.uint16)]
+
+
 def is_nonfinite16(bits: np.ndarray, fmt: str) -> np.ndarray:
     """True where the pattern is +-inf or NaN (exponent field all ones)."""
     ebits, mbits, _, emax_field, _, _ = _fields(fmt)
@@ -48,9 +60,30 @@ def is_nonfinite16(bits: np.ndarray, fmt: str) -> np.ndarray:
     return ((b >> mbits) & emax_field) == emax_field
 
 
+def _encode_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """bfloat16 is the upper half of a binary32 pattern (same sign and
+    exponent fields, the top 7 fraction bits), so rounding a float32 to it is
+    rounding its pattern to a multiple of 2^16: keep the upper 16 bits and add
+    one when the dropped lower 16 bits exceed half (0x8000), or equal half
+    while the kept part is odd.  A carry out of the fraction moves into the
+    next binade, and past the largest finite value into the infinity pattern,
+    as round-to-nearest requires.  NaN becomes the quiet NaN of its sign."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32, order="C")
+    u = x32.view(np.uint32)
+    upper, lower = u >> np.uint32(16), u & np.uint32(0xFFFF)
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & np.uint32(1)) == 1))
+    out = (upper + up).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0) | (upper[nan] & np.uint32(0x8000)).astype(np.uint16)
+    return out
+
+
 def encode16_rne(x: np.ndarray, fmt: str) -> np.ndarray:
     """Round float values (float32 or exactly float32-representable float64)
     to the nearest 16-bit value, ties to even; return raw uint16 bits."""
+    if fmt == "bf16":
+        return _encode_bf16_rne(x)
     ebits, mbits, bias, emax_field, emin, emax = _fields(fmt)
     x = np.asarray(x, dtype=np.float64)
     neg = np.signbit(x)
