@@ -6,7 +6,9 @@ reduction and norm kernels must carry the non-temporal hint.  This is the layout
 kernels were measured in: a loop transformation in the compiler once
 promoted the AdamW stores out of a one-iteration loop and dropped the hint,
 costing about 10 points of HBM bandwidth without changing any result.  No
-kernel may use scratch memory (register spills).
+kernel may use scratch memory (register spills).  The AdamW kernels round
+the 16-bit parameter from the stored float32 master: no fused fp16 mix
+instruction (which would round the unrounded fma result instead).
 """
 import os
 import re
@@ -74,3 +76,18 @@ def test_no_kernel_spills(kernels):
     for name, (_, meta) in kernels.items():
         m = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta)
         assert m and int(m.group(1)) == 0, f"{name} uses scratch memory"
+
+
+def test_adamw_writeback_rounds_the_stored_master(kernels):
+    """v_fma_mixlo/mixhi_f16 (or v_mad_mix*) writing fp16 would round the
+    update's exact fma result to the parameter copy, skipping the float32
+    rounding of the stored master (one ulp apart in about 6 of 100,000
+    parameters).  Only the plain conversions may form the copy."""
+    checked = 0
+    for name, (body, _) in kernels.items():
+        if _kind(name) not in ("adam_update", "adam_update_devcoef"):
+            continue
+        fused = re.findall(r"^\s*(v_(?:fma|mad)_mix(?:lo|hi)_f16)\b", body, re.M)
+        assert not fused, f"{name}: {len(fused)} fused fp16 conversions"
+        checked += 1
+    assert checked >= 8

@@ -162,9 +162,15 @@ __device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
 }
 
 // round-to-nearest-even float -> 16-bit bits (hardware conversion under the
-// default round-to-nearest-even mode: v_cvt_f16_f32 / v_cvt_pk_bf16_f32)
+// default round-to-nearest-even mode: v_cvt_f16_f32 / v_cvt_pk_bf16_f32).
+// x is the float32 master as stored.  The empty asm makes it an opaque
+// register value, so the compiler cannot fuse the conversion into the
+// arithmetic that produced it: a fused v_fma_mixlo_f16 rounds the unrounded
+// result straight to fp16, which differs from rounding the stored float32
+// master in the rare cases where the two roundings meet a tie.
 template <int DT>
 __device__ __forceinline__ uint32_t to16(float x) {
+    __asm__("" : "+v"(x));
     if constexpr (DT == ZERO_F16) {
         return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
     } else {
