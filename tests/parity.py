@@ -53,9 +53,22 @@ def ordered16(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
-def check_param(name, got_bits, ref_bits, max_ulp=1):
+def _value16(bits: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_param(name, got_bits, ref_bits, max_ulp=1, fmt=None, abs_=ABS):
+    """At most max_ulp apart on the ordered-integer line; with fmt given,
+    pairs further apart pass if their values differ by at most abs_ (near
+    zero the parameter copy inherits the master's absolute floor)."""
+    got_bits = np.asarray(got_bits, np.uint16)
+    ref_bits = np.asarray(ref_bits, np.uint16)
     d = np.abs(ordered16(got_bits) - ordered16(ref_bits))
     bad = d > max_ulp
+    if fmt is not None and bad.any():
+        bad &= ~(np.abs(_value16(got_bits, fmt) - _value16(ref_bits, fmt)) <= abs_)
     if bad.any():
         i = np.flatnonzero(bad)[:5]
         raise AssertionError(f"{name}: {bad.sum()} params more than {max_ulp} ulp off; idx {i.tolist()} "
