@@ -131,18 +131,19 @@ def _oracle_worker(job):
     return sum(n for _, n in blocks), spent
 
 
-def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, max_procs=16, reduce=0):
+def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, reduce=0):
     """The CPU oracle timed on a bounded sample of the same shard, blocks of
     consecutive parameters from its start, one step per block:
-      all cores  one process per host core (at most `max_procs`), two blocks
-                 of `par_block` each; rate = sampled params / the busiest
-                 process's oracle time;
+      all cores  one process per host core this process may run on (its
+                 affinity set), two blocks of `par_block` each; rate =
+                 sampled params / the busiest process's oracle time;
       one core   one process, blocks of `block` until `target_s` seconds of
                  oracle time.
     Runs before the GPU is touched (workers are forked)."""
     import multiprocessing
 
-    cores = max(1, min(max_procs, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, affinity)
     nblk = min(2 * cores, -(-S // par_block))
     blocks = [(begin + k * par_block, min(par_block, S - k * par_block)) for k in range(nblk)]
     jobs = [(w, blocks[j::cores], accum, reduce) for j in range(cores) if blocks[j::cores]]
@@ -157,9 +158,12 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1
         done += n
     what = f"{accum} accumulations + " if accum else f"reduction of {reduce} slices + " if reduce else ""
     return {"value": par_done / par_time, "unit": "params/s", "cores": len(jobs), "kind": "oracle",
+            "host_cores_affinity": affinity, "host_cpu_count": os.cpu_count(),
             "sample": f"first {par_done} of the shard's {S} params in blocks of {par_block}, one step each "
                       f"({what}exact norm + AdamW, float64 NumPy), {len(jobs)} processes of one thread "
-                      f"each; busiest process {par_time:.1f} s of oracle time, input generation excluded",
+                      f"each, one per host core of the {affinity} this process may run on "
+                      f"(os.cpu_count() {os.cpu_count()}); busiest process {par_time:.1f} s of oracle time, "
+                      f"input generation excluded",
             "one_core": {"value": done / spent, "cores": 1,
                          "sample": f"first {done} params in blocks of {block}, one process, {spent:.1f} s of "
                                    f"oracle time"}}
@@ -247,6 +251,9 @@ def main():
                     help="keep the loss scaler and step counter on the host, reading the 4-byte overflow flag back "
                          "every step (default: both live in device memory and no step waits for the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-workload", default="gpt100b",
+                    help="a second workload timed after the headline one on the default path and reported under "
+                         "extra_workload ('' to skip; ignored with --accum/--reduce/--graph/--host-scaler)")
     ap.add_argument("--alloc", choices=["contiguous", "torch"], default="contiguous",
                     help="where the shard's buffers come from: physically contiguous HBM through the library's "
                          "allocator in a torch memory pool (default), or torch's default allocator")
@@ -283,14 +290,106 @@ def main():
 
     import zero_sharded_mixed_partition_amd as Z
     torch.cuda.set_device(0)
+    K = args.accum
+    R = args.reduce
+    res = run_shard(w, args, K, R, args.steps, args.warmup)
+    S, ms_step = res["S"], res["ms_step"]
+
+    # the achievable rate of one read + one write stream over the same 14 B/param
+    # each way (at most 16 GiB): the library's reference copy kernel, and
+    # torch's device-to-device copy (the runtime's blit kernel, also the
+    # known-size copy that scales the HBM byte counters)
+    cbytes = min(S * 14, 16 << 30) // 16 * 16
+    src = torch.empty(cbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def time_copy(fn):
+        for _ in range(3):
+            fn()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            fn()
+        c1.record()
+        torch.cuda.synchronize()
+        return 2 * cbytes / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+
+    ref_gbps = time_copy(lambda: Z.zero_copy_reference(dst, src, cbytes))
+    copy_gbps = time_copy(lambda: dst.copy_(src))
+    del src, dst
+
+    # the second workload at the target shard sizes, as extra keys: one rank's
+    # 250M-parameter shard of a 100B model, applied and skipped steps timed
+    # on the same path (default run only; the headline value stays the one above)
+    extra = None
+    if args.extra_workload and not (K or R or args.graph or args.host_scaler):
+        w2 = W.get(args.extra_workload)
+        if w2.name != w.name:
+            r2 = run_shard(w2, args, 0, 0, args.steps, args.warmup)
+            extra = {"workload": w2.name, "shard_params": r2["S"], "n_d": w2.n_d, "rank": w2.rank,
+                     "grad_dtype": w2.grad_dtype, "param_dtype": w2.param_dtype, "steps": args.steps,
+                     "ms_per_step": r2["ms_step"], "params_per_s": r2["S"] / (r2["ms_step"] * 1e-3),
+                     "hbm_gbps": r2["step_gbps"], "hbm_frac_of_peak": r2["step_gbps"] / PEAK_HBM_GBPS,
+                     "step_ms": r2["step_ms"], "buffers": r2["buffers"],
+                     "update": {"kernel": r2["roofline"]["kernel"], "avg_ms": r2["roofline"]["avg_ms"],
+                                "gbps": r2["roofline"]["achieved"], "frac": r2["roofline"]["frac"],
+                                "traffic": r2["roofline"]["traffic"]},
+                     "norm_pass": r2["norm_pass"], "skipped_step": r2["skipped_step"]}
+
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shard_params": S, "n_d": w.n_d, "rank": w.rank,
+                   "flat_offset": res["begin"], "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
+                   "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
+                   "weight_decay": w.weight_decay, "param_layout": w.param_layout,
+                   "path": res["path"], "algorithmic_bytes_per_param": res["step_bpp"],
+                   "buffers": res["buffers"]},
+        "hbm_gbps": res["step_gbps"],
+        "hbm_frac_of_peak": res["step_gbps"] / PEAK_HBM_GBPS,
+        "roofline": res["roofline"],
+        "step_ms": res["step_ms"],
+        "norm_pass": res["norm_pass"],
+        "skipped_step": res["skipped_step"],
+        "copy_reference": {"kernel": "copy16 (zero_copy_reference)", "bytes_each_way": cbytes, "gbps": ref_gbps,
+                           "frac_of_peak": ref_gbps / PEAK_HBM_GBPS,
+                           "adam_update_frac_of_copy": res["roofline"]["achieved"] / ref_gbps,
+                           "step_frac_of_copy": res["step_gbps"] / ref_gbps},
+        "accumulate": res["accumulate"],
+        "reduce": res["reduce"],
+        "torch_copy_gbps": copy_gbps,
+        "skipped_steps": res["skipped"],
+        "extra_workload": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_shard(w, args, K, R, steps, warmup):
+    """Uploads workload w's shard, runs `warmup` untimed and `steps` timed
+    steps (a synchronize on both sides of the timed region), then 10 skipped
+    steps timed apart; frees the shard and returns the measurements."""
+    import torch
+
+    import zero_sharded_mixed_partition_amd as Z
     offsets, S, padded = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
     begin = w.rank * S
     print(f"# workload {w.name}: shard {S} params at flat offset {begin}", file=sys.stderr, flush=True)
     # the shard's streams: physically contiguous HBM by default (the update
-    # kernel's rate depends on where its eight streams' pages land)
+    # kernel's rate depends on where its eight streams' pages land); the
+    # library counts the segments it hands out, so the label says what they got
     pool_ctx = torch.cuda.use_mem_pool(Z.contiguous_pool()) if args.alloc == "contiguous" else contextlib.nullcontext()
-    K = args.accum
-    R = args.reduce
+    pool0 = Z.zero_pool_counts()
     with pool_ctx:
         P, M, V, G = upload_inputs(w, begin, S, w.grad_dtype)
         pdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.param_dtype]
@@ -298,13 +397,24 @@ def main():
         A = torch.empty(S, dtype=torch.float32, device="cuda") if (K or R) else None
         # the other ranks' slices: copies of this rank's gradient (distinct buffers, same values)
         slices = [G] + [G.clone() for _ in range(R - 1)] if R else None
+    pool1 = Z.zero_pool_counts()
+    n_contig, n_fallback = pool1[0] - pool0[0], pool1[1] - pool0[1]
+    if args.alloc != "contiguous":
+        buffers = "torch default allocator"
+    elif pool1[1] == 0:
+        buffers = (f"physically contiguous HBM (library allocator behind a torch memory pool: {pool1[0]} segments "
+                   f"so far, {n_contig} new for this shard, none fell back to ordinary memory)")
+    else:
+        buffers = (f"library allocator behind a torch memory pool: {pool1[1]} of its {pool1[0] + pool1[1]} segments "
+                   f"({n_fallback} of {n_contig + n_fallback} new for this shard) fell back to ordinary device "
+                   f"memory, the rest physically contiguous")
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                       max_grad_norm=w.max_grad_norm,
                       scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)),
                       applied_steps=w.step - 1, graph=args.graph,
                       device_state=not args.host_scaler)
     DS = opt.state is not None
-    FUSED = bool(args.accum or args.reduce) and not args.separate_norm
+    FUSED = bool(K or R) and not args.separate_norm
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -348,16 +458,16 @@ def main():
             ev[2].record()
         return opt.finish()                    # device_state: None, nothing waits
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     skipped = 0
     wall = []
     skipped0 = opt.read_state().skipped if DS else 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         ts = time.perf_counter()
         if args.graph:
             evs[k][6].record()
@@ -372,21 +482,21 @@ def main():
     if DS:
         # nothing waited inside the loop: per-step times from the events, start to next start
         starts = [e[6] for e in evs]
-        wall = [starts[k].elapsed_time(starts[k + 1]) * 1e-3 for k in range(args.steps - 1)]
+        wall = [starts[k].elapsed_time(starts[k + 1]) * 1e-3 for k in range(steps - 1)]
         wall.append(starts[-1].elapsed_time(evs[-1][2]) * 1e-3)
         skipped = opt.read_state().skipped - skipped0
-    print(f"# timed {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"# timed {steps} steps", file=sys.stderr, flush=True)
     if args.graph:
         # a replayed graph has no events between its kernels: the per-kernel
         # times come from the same kernels launched one by one, after the
         # timed region
-        for k in range(args.steps):
+        for k in range(steps):
             step(evs[k])
         torch.cuda.synchronize()
 
     # skipped steps, timed apart: +inf in one gradient element makes the norm
     # pass raise the flag and the update exit without touching the state
-    n_skip = min(10, args.steps)
+    n_skip = min(10, steps)
     keep = G[S // 2].clone()
     G[S // 2] = float("inf")
     sev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_skip)]
@@ -406,7 +516,7 @@ def main():
     G[S // 2] = keep
     torch.cuda.synchronize()
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = (t1 - t0) * 1e3 / steps
     norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     adam_ms = sorted(e[5].elapsed_time(e[2]) for e in evs)
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
@@ -437,59 +547,18 @@ def main():
                         "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
                         "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9,
                         "traffic": measured_traffic(run_key, "grad_sum_norm" if FUSED else "grad_reduce")}
-
-    # the achievable rate of one read + one write stream over the same 14 B/param
-    # each way (at most 16 GiB): the library's reference copy kernel, and
-    # torch's device-to-device copy (the runtime's blit kernel, also the
-    # known-size copy that scales the HBM byte counters)
-    cbytes = min(S * 14, 16 << 30) // 16 * 16
-    src = torch.empty(cbytes // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-
-    def time_copy(fn):
-        for _ in range(3):
-            fn()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(10):
-            fn()
-        c1.record()
-        torch.cuda.synchronize()
-        return 2 * cbytes / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
-
-    ref_gbps = time_copy(lambda: Z.zero_copy_reference(dst, src, cbytes))
-    copy_gbps = time_copy(lambda: dst.copy_(src))
-    del src, dst
-
+    path = ((f"fp32 gradient accumulation, {K} micro-batches" if K else
+             f"reduction of {R} ranks' 16-bit slices into the fp32 copy" if R else "16-bit gradient")
+            + ((", norm in the pass that writes the copy" if FUSED else ", separate norm pass") if (K or R) else "")
+            + (", recorded step graph" if args.graph else "")
+            + (", scaler and step counter in device memory" if DS else ", host loss scaler (4-byte flag read per step)"))
     out = {
-        "metric": METRIC,
-        "value": S / (ms_step * 1e-3),
-        "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "shard_params": S, "n_d": w.n_d, "rank": w.rank,
-                   "flat_offset": begin, "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype,
-                   "state_dtype": "f32", "step_t": w.step, "clip_max_norm": w.max_grad_norm,
-                   "weight_decay": w.weight_decay, "param_layout": w.param_layout,
-                   "path": (f"fp32 gradient accumulation, {K} micro-batches" if K else
-                            f"reduction of {R} ranks' 16-bit slices into the fp32 copy" if R else "16-bit gradient")
-                   + ((", norm in the pass that writes the copy" if FUSED else ", separate norm pass") if (K or R) else "")
-                   + (", recorded step graph" if args.graph else "")
-                   + (", scaler and step counter in device memory" if DS else ", host loss scaler (4-byte flag read per step)"),
-                   "algorithmic_bytes_per_param": step_bpp,
-                   "buffers": ("physically contiguous HBM (library allocator behind a torch memory pool)"
-                               if args.alloc == "contiguous" else "torch default allocator")},
-        "hbm_gbps": step_gbps,
-        "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
-        "roofline": {"bound": "hbm", "kernel": "adam_update_devcoef" if DS else "adam_update", "achieved": adam_gbps, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+        "S": S, "begin": begin, "ms_step": ms_step, "step_bpp": step_bpp, "step_gbps": step_gbps,
+        "path": path, "buffers": buffers, "skipped": skipped,
+        "roofline": {"bound": "hbm", "kernel": "adam_update_devcoef" if DS else "adam_update", "achieved": adam_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+                     "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, profiles/hbm_counters.json, "
+                                        "taken on the same kernel code (hash match)") if traffic else None,
                      "algorithmic_bytes": adam_bpp * S, "avg_ms": adam_avg,
                      "p10_ms": pct(adam_ms, 0.1), "p90_ms": pct(adam_ms, 0.9),
                      "timed_on": "eager launches after the timed region" if args.graph else "the timed steps"},
@@ -500,16 +569,12 @@ def main():
         "skipped_step": {"steps": n_skip, "ms_per_step": mean(skip_wall) * 1e3,
                          "norm_ms": mean([e[0].elapsed_time(e[1]) for e in sev]),
                          "update_ms": mean([e[5].elapsed_time(e[2]) for e in sev])},
-        "copy_reference": {"kernel": "copy16 (zero_copy_reference)", "bytes_each_way": cbytes, "gbps": ref_gbps,
-                           "frac_of_peak": ref_gbps / PEAK_HBM_GBPS, "adam_update_frac_of_copy": adam_gbps / ref_gbps,
-                           "step_frac_of_copy": step_gbps / ref_gbps},
         "accumulate": accum_stats,
         "reduce": reduce_stats,
-        "torch_copy_gbps": copy_gbps,
-        "skipped_steps": skipped,
-        "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    del opt, P, M, V, G, par, A, slices
+    torch.cuda.synchronize()
+    return out
 
 
 if __name__ == "__main__":

@@ -19,6 +19,24 @@
  *  decoupled weight decay scaled by the learning rate (Loshchilov & Hutter
  *  2019), and round-to-nearest-even writeback of the 16-bit parameter copy.
  *
+ * The step's contract is eight calls: zero_partition_plan and
+ * zero_rank_fragments (the plan), zero_norm_workspace_bytes and
+ * zero_shard_unscale_norm_overflow (steps 1-2), zero_shard_adam_step (steps
+ * 3-4), zero_loss_scaler_update (the scalar decision), zero_status_string and
+ * zero_last_error.  They allocate nothing and keep no state besides the
+ * thread-local error string.  Every other call is an extra on the same
+ * kernels, marked where it is declared:
+ *  - the same step with its coefficients or its scaler state in caller-owned
+ *    device memory (zero_adam_prepare, *_coef, *_dev, zero_step_decide_dev,
+ *    zero_shard_norm_decide_dev);
+ *  - recorded step graphs (zero_step_graph_*), which ALLOCATE at create;
+ *  - the rows around the step: fp32 gradient accumulation, the reduction of
+ *    the ranks' gradient slices, the copy-and-norm pass, the combine of the
+ *    ranks' scalars, and the step on host cores (whose worker threads start
+ *    on first use and live until the process ends);
+ *  - physically contiguous memory (zero_device_alloc_contiguous, zero_pool_*),
+ *    whose purpose is to allocate, and the measurement copy.
+ *
  * Conventions for every function:
  *  - Returns an int status: ZERO_OK (0) or a negative zero_status (the
  *    pool allocator pair excepted, whose signatures torch fixes).  Nothing
@@ -33,8 +51,7 @@
  *    calls near the end of this header, whose purpose is to allocate.
  *  - The caller owns every host array and device buffer.  Device pointers
  *    must point to device memory of the current HIP device and be 16-byte
- *    aligned (ZERO_EALIGN otherwise).  The library keeps no state apart from
- *    the thread-local error string.
+ *    aligned (ZERO_EALIGN otherwise).
  *  - Sizes are element counts in int64; n = 0 is a valid no-op.
  */
 #ifndef ZERO_SHARD_H
@@ -114,6 +131,15 @@ int zero_rank_fragments(const int64_t* dims, const int32_t* ndims, int32_t n_ten
 
 /* ---------------------------------------------------------------------------
  * Step 1+2: unscale, inf/NaN detection, squared L2 norm of one gradient shard.
+ * Contract call.
+ *
+ * Passages: the gradient shard is the 2-byte gradient of mixed-precision
+ * Adam's per-parameter state (explainer, "The 16 Bytes per Parameter Audit";
+ * Ch.02 "The Three Stages", memory per parameter), and under P_os+g each rank
+ * holds only its partition of it (Ch.02, what each stage shards).  The pages
+ * name mixed precision but not loss scaling or clipping: unscaling by the
+ * loss scale with an inf/NaN skip follows Micikevicius et al. 2018, the
+ * squared norm feeds max-norm clipping (Pascanu et al. 2013).
  *
  *  grad        device, [n] values of format grad_dtype: 16-bit raw bits
  *              (ZERO_F16, ZERO_BF16) or fp32 (ZERO_F32)
@@ -145,6 +171,15 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
 
 /* ---------------------------------------------------------------------------
  * Steps 3+4: fused Adam/AdamW update of one shard and 16-bit writeback.
+ * Contract call.
+ *
+ * Passages: each rank updates the fp32 master, momentum and variance of its
+ * own partition only and writes the 2-byte weight copy of it (ZeRO method
+ * entry, description; explainer, "The 16 Bytes per Parameter Audit" and
+ * Ch.02 "The Three Stages", memory per parameter and what each stage shards;
+ * History, "The mixed-precision era").  The update rule, which the pages do
+ * not print, is bias-corrected Adam (Kingma & Ba 2015) with decoupled weight
+ * decay (Loshchilov & Hutter 2019).
  *
  * Hyperparameters are double; the host derives the per-step float32
  * coefficients from them in double and rounds each once.  `step` is the
@@ -189,7 +224,8 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
                          const int32_t* d_global_overflow, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * Coefficients in device memory, and recorded step graphs.
+ * Coefficients in device memory, and recorded step graphs.  Extras: the
+ * coefficient block in device memory, and graphs that allocate at create.
  *
  * zero_adam_prepare writes the per-step coefficient block that
  * zero_shard_adam_step derives from hp (zero_adam_coef_bytes() bytes of
@@ -238,6 +274,7 @@ int zero_step_graph_destroy(zero_step_graph* g);
 /* ---------------------------------------------------------------------------
  * Gradient accumulation into an fp32 copy (explainer, Ch.02 "The Three
  * Stages", memory per parameter: an fp16 gradient plus its fp32 copy).
+ * Extra: the fp32-accumulation row around the step.
  * For each micro-batch:  acc = (first ? 0 : acc) + grad * inv_loss_scale,
  * in fp32 with one rounding per element (fused multiply-add).
  *
@@ -259,8 +296,9 @@ int zero_shard_grad_accumulate(float* acc, const void* grad, int32_t grad_dtype,
 
 /* ---------------------------------------------------------------------------
  * Reduction of this partition's gradient over the data-parallel ranks: the
- * local half of a gradient reduce-scatter.  Plain data parallelism sums the
- * ranks' gradients (explainer, History, "Data parallelism's reign"); once
+ * local half of a gradient reduce-scatter (extra: a row around the step).
+ * Plain data parallelism sums the ranks' gradients (explainer, History,
+ * "Data parallelism's reign"); once
  * gradients are partitioned each rank keeps the reduced gradient of its own
  * partition only (explainer, Ch.02 "The Three Stages", what each stage shards,
  * and the stage table: reduce-scatter).  A direct reduce-scatter delivers the
@@ -288,8 +326,9 @@ int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slic
                            int64_t n, double inv_loss_scale, int32_t* d_overflow, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * The same step on host cores, for optimizer states kept in host memory (the
- * CPU-offload lineage: explainer, Legacy, "The trillion-parameter claim";
+ * Extra: the same step on host cores, for optimizer states kept in host
+ * memory (the CPU-offload lineage: explainer, Legacy, "The trillion-parameter
+ * claim";
  * glossary description, CPU offloading).  All pointers are HOST pointers
  * (pinned or pageable); the calls are synchronous and return when done.
  * They compute what the device entry points compute, from the same per-step
@@ -316,7 +355,11 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
                              int32_t global_overflow, int32_t nthreads);
 
 /* ---------------------------------------------------------------------------
- * Step 2 (scalar, host): dynamic loss scale update after a step.
+ * Step 2 (scalar, host): dynamic loss scale update after a step.  Contract
+ * call.  Passage: the pages name mixed-precision (fp16) training
+ * (explainer, History, "The mixed-precision era") but not its loss scaling;
+ * the dynamic scale with back-off on overflow and growth after a run of clean
+ * steps follows Micikevicius et al. 2018.
  * On overflow: *skip_out = 1, scale = max(scale*backoff, min_scale),
  * good_steps = 0.  Otherwise *skip_out = 0, good_steps += 1 and, when it
  * reaches growth_interval, scale *= growth and good_steps = 0.
@@ -334,6 +377,8 @@ int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip
 
 /* ---------------------------------------------------------------------------
  * The step with its scalar state in device memory: no host round trip.
+ * Extras: the contract's steps with the scaler state in caller-owned device
+ * memory.
  *
  * The loss scaler and the step counts live in a zero_step_state in device
  * memory.  The norm pass reads the loss scale from it; a one-thread kernel,
@@ -425,7 +470,7 @@ int zero_step_graph_launch_dev(zero_step_graph* g, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * The fp32 gradient copy and its norm in one pass (fp32 accumulation and the
- * local half of the reduce-scatter above, fused with the norm pass).
+ * local half of the reduce-scatter above, fused with the norm pass).  Extra.
  *
  * zero_shard_grad_sum_norm writes
  *     acc = (add_to_acc ? acc : 0) + sum_k slices[k] * inv_loss_scale,
@@ -463,20 +508,22 @@ int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t 
                                  void* d_workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * Measurement aid (not a step of the method): a plain device copy, one
+ * Extra, a measurement aid (not a step of the method): a plain device copy, one
  * 16-byte vector per lane, in the same streaming style as the step's kernels.
  * Its rate is the achievable rate of one read plus one write stream, which
  * the step's kernels are reported against beside the nominal HBM peak.
  * Async on hip_stream.  dst, src: device, 16-byte aligned, not overlapping;
- * bytes: a multiple of 16 (0 is a no-op).
- * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP.
+ * bytes: a multiple of 16 (0 is a no-op), any size (one launch; past 64 GiB
+ * its lanes loop).
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_EHIP.
  * ------------------------------------------------------------------------- */
 int zero_copy_reference(void* dst, const void* src, int64_t bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * The local half of the all-reduce of the norm pass's two scalars: the one
- * exchange inside the step.  Each rank updates only its own partition (ZeRO
- * method entry, description; explainer, Ch.02 "The Three Stages", what each
+ * exchange inside the step (extra: a row around the step).  Each rank
+ * updates only its own partition (ZeRO method entry, description;
+ * explainer, Ch.02 "The Three Stages", what each
  * stage shards), while the clip coefficient and the skip depend on the whole
  * gradient: the data-parallel sum of the ranks' sums of squares and the OR of
  * their inf/NaN flags.  With a direct exchange every rank writes its
@@ -499,8 +546,8 @@ int zero_norm_combine_ranks(const double* slot_sqnorm, const int32_t* slot_overf
                             double* d_global_sqnorm, int32_t* d_global_overflow, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
- * Physically contiguous device memory for a shard's streams (a layout choice
- * for HBM, not a step of the method).  The fused AdamW pass streams four
+ * Extras: physically contiguous device memory for a shard's streams (a
+ * layout choice for HBM, not a step of the method).  The fused AdamW pass streams four
  * buffers in and four out at once, and its rate depends on where their pages
  * land.  On one MI355X, over 16 processes each, buffers from the default
  * allocator ran at 75-82% of the 8 TB/s peak (mean 79.5%).  Physically
@@ -518,12 +565,18 @@ int zero_norm_combine_ranks(const double* slot_sqnorm, const int32_t* slot_overf
  *   pool that serves the shard's tensors.  zero_pool_alloc falls back to
  *   ordinary device memory when no contiguous range is left and returns NULL
  *   only when that fails too.  The stream argument is unused.
- * These four calls and the step graphs are the only ones that allocate.
+ * zero_pool_counts: how many segments zero_pool_alloc has handed out since
+ *   the library was loaded, physically contiguous (*contiguous) and fallen
+ *   back to ordinary device memory (*fallback), over all devices.  These two
+ *   process-wide counters are the library's only state besides the
+ *   thread-local error string.  Errors: ZERO_EINVAL (NULL output).
+ * These calls and the step graphs are the only ones that allocate.
  * ------------------------------------------------------------------------- */
 int zero_device_alloc_contiguous(void** ptr, size_t bytes);
 int zero_device_free(void* ptr);
 void* zero_pool_alloc(size_t bytes, int device, void* stream);
 void zero_pool_free(void* ptr, size_t bytes, int device, void* stream);
+int zero_pool_counts(int64_t* contiguous, int64_t* fallback);
 
 /* Static description of a status code, and the thread-local detail of the
  * last failing call (empty string if none). */

@@ -40,3 +40,15 @@ def test_bench_json_line(extra):
         assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == "params/s"
     if "--reduce" in extra:
         assert d["reduce"]["slices"] == 3 and d["reduce"]["gbps"] > 0
+    # the shard's buffers come from the library's contiguous pool; the label
+    # says whether any segment fell back to ordinary memory
+    assert d["config"]["buffers"].startswith("physically contiguous HBM") and "none fell back" in d["config"]["buffers"]
+    if not extra:
+        # default path: the 100B model's 250M-parameter rank shard is timed as well
+        x = d["extra_workload"]
+        assert x["workload"] == "gpt_100b_nd400_rank200" and x["shard_params"] == 250_749_440
+        assert x["ms_per_step"] > 0 and 0 < x["update"]["frac"] < 1.1 and x["skipped_step"]["steps"] == 5
+        cb = d["cpu_baseline"]
+        assert 1 <= cb["cores"] <= cb["host_cores_affinity"] <= cb["host_cpu_count"]
+    else:
+        assert d["extra_workload"] is None

@@ -35,7 +35,7 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
            "zero_shard_norm_decide_dev", "StepGraphDev", "zero_sum_norm_workspace_bytes", "zero_shard_grad_sum_norm",
            "zero_shard_grad_sum_norm_dev", "zero_device_alloc_contiguous", "zero_device_free",
-           "contiguous_pool"]
+           "zero_pool_counts", "contiguous_pool"]
 
 
 def zero_abi_version() -> int:
@@ -609,6 +609,15 @@ def zero_device_alloc_contiguous(nbytes: int) -> int:
 
 def zero_device_free(ptr: int) -> None:
     _L.check(_L.lib().zero_device_free(ptr or None), "zero_device_free")
+
+
+def zero_pool_counts():
+    """(contiguous, fallback): how many segments zero_pool_alloc has handed
+    out since the library was loaded, physically contiguous and fallen back
+    to ordinary device memory."""
+    c, f = ctypes.c_int64(), ctypes.c_int64()
+    _L.check(_L.lib().zero_pool_counts(ctypes.byref(c), ctypes.byref(f)), "zero_pool_counts")
+    return c.value, f.value
 
 
 _POOLS = {}

@@ -81,6 +81,7 @@ SIGNATURES = {
     "zero_device_free": (c_i32, [c_vp]),
     "zero_pool_alloc": (c_vp, [c_sz, c_i32, c_vp]),
     "zero_pool_free": (None, [c_vp, c_sz, c_i32, c_vp]),
+    "zero_pool_counts": (c_i32, [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
     "zero_norm_combine_ranks": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "zero_shard_unscale_norm_overflow_dev": (c_i32, [c_vp, c_i32, c_i64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "zero_shard_norm_decide_dev": (c_i32, [c_vp, c_i32, c_i64, ctypes.POINTER(zero_adam_hyper), c_vp, c_vp, c_vp,

@@ -6,9 +6,12 @@
 // Each lane moves one 16-byte vector; a wave's load and store instructions
 // each cover one contiguous 1 KiB run.  One-shot grid of 256-thread
 // workgroups in address order; non-temporal hints on both sides, as in the
-// step's kernels.
+// step's kernels.  A launch holds fewer than 2^32 work-items, so a copy past
+// 2^24 - 1 workgroups' worth (just under 64 GiB) takes further turns of a
+// grid-stride loop.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "common.h"
@@ -20,12 +23,14 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCopyThreads = 256;
-constexpr int64_t kCopyMaxGrid = (int64_t(1) << 31) - 1;
+// grid * kCopyThreads stays below 2^32 work-items per dispatch
+constexpr int64_t kCopyMaxGrid = (int64_t(1) << 24) - 1;
 
 __global__ __launch_bounds__(kCopyThreads) void copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                        int64_t nvec) {
-    const int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
-    if (i < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < nvec; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
@@ -41,8 +46,7 @@ extern "C" int zero_copy_reference(void* dst, const void* src, int64_t bytes, vo
     if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15u)
         return fail(ZERO_EALIGN, "dst and src must be 16-byte aligned");
     const int64_t nvec = bytes / 16;
-    const int64_t grid = (nvec + kCopyThreads - 1) / kCopyThreads;
-    if (grid > kCopyMaxGrid) return fail(ZERO_ERANGE, "copy too large for one launch");
+    const int64_t grid = std::min<int64_t>((nvec + kCopyThreads - 1) / kCopyThreads, kCopyMaxGrid);
     const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
     if (d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) return fail(ZERO_EINVAL, "dst and src overlap");
     hipLaunchKernelGGL(copy16, dim3((unsigned)grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(hip_stream),

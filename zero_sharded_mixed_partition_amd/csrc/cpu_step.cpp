@@ -1,7 +1,8 @@
 // Host (CPU) implementation of one rank's shard step, for optimizer states
-// kept in host memory: the CPU-offload lineage that the explainer's Legacy
-// section names ("ZeRO-Infinity extended the ladder to CPU/NVMe offload") and
-// the glossary lists among ZeRO's companions (CPU offloading).  The step is
+// kept in host memory: the CPU-offload lineage (explainer "Data Parallelism
+// Without the Copies", Legacy, card "The trillion-parameter claim": later
+// work carried the stages on to offloading into CPU memory and NVMe; the
+// glossary entry's description lists CPU offloading beside ZeRO).  The step is
 // the same one the device kernels compute (unscale, inf/NaN test, squared
 // norm; clip; bias-corrected AdamW; 16-bit writeback), with the per-step
 // coefficients from the same host routine, on host cores over host memory.

@@ -13,7 +13,9 @@
 // pluggable allocator, so a torch memory pool can serve tensors from it.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
+#include <cstdint>
 
 #include "common.h"
 #include "zero_shard.h"
@@ -21,6 +23,13 @@
 using namespace zero_shard;
 
 namespace {
+
+// What zero_pool_alloc has handed out since the library was loaded: segments
+// that are physically contiguous, and segments that fell back to ordinary
+// device memory.  Read by zero_pool_counts, so a caller can tell which kind
+// its tensors got.
+std::atomic<int64_t> g_pool_contiguous{0};
+std::atomic<int64_t> g_pool_fallback{0};
 
 // Allocates on `device` (the current device if device < 0), restoring the
 // caller's current device.
@@ -72,13 +81,27 @@ void* zero_pool_alloc(size_t bytes, int device, void* stream) {
     (void)stream;
     if (bytes == 0) return nullptr;
     void* p = nullptr;
-    if (alloc_on(&p, bytes, device, true) == hipSuccess) return p;
+    if (alloc_on(&p, bytes, device, true) == hipSuccess) {
+        g_pool_contiguous.fetch_add(1, std::memory_order_relaxed);
+        return p;
+    }
     // no contiguous range of that size left: ordinary device memory
     (void)hipGetLastError();
     p = nullptr;
-    if (alloc_on(&p, bytes, device, false) == hipSuccess) return p;
+    if (alloc_on(&p, bytes, device, false) == hipSuccess) {
+        g_pool_fallback.fetch_add(1, std::memory_order_relaxed);
+        return p;
+    }
     (void)hipGetLastError();
     return nullptr;
+}
+
+int zero_pool_counts(int64_t* contiguous, int64_t* fallback) {
+    clear_error();
+    if (contiguous == nullptr || fallback == nullptr) return fail(ZERO_EINVAL, "output pointer is NULL");
+    *contiguous = g_pool_contiguous.load(std::memory_order_relaxed);
+    *fallback = g_pool_fallback.load(std::memory_order_relaxed);
+    return ZERO_OK;
 }
 
 void zero_pool_free(void* ptr, size_t bytes, int device, void* stream) {
