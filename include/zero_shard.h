@@ -28,7 +28,9 @@
  * kernels, marked where it is declared:
  *  - the same step with its coefficients or its scaler state in caller-owned
  *    device memory (zero_adam_prepare, *_coef, *_dev, zero_step_decide_dev,
- *    zero_shard_norm_decide_dev);
+ *    zero_shard_norm_decide_dev) and the norm pass without a workspace
+ *    (zero_shard_unscale_norm_overflow_noalloc, which uses a fixed array the
+ *    library keeps on each GPU);
  *  - recorded step graphs (zero_step_graph_*), which ALLOCATE at create;
  *  - the rows around the step: fp32 gradient accumulation, the reduction of
  *    the ranks' gradient slices, the copy-and-norm pass, the combine of the
@@ -168,6 +170,23 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
                                      double inv_loss_scale, double* d_sqnorm,
                                      int32_t* d_overflow, void* d_workspace,
                                      size_t workspace_bytes, void* hip_stream);
+
+/* zero_shard_unscale_norm_overflow without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The norm pass's block
+ * partials live in a fixed 8 KiB array in device memory that the library
+ * holds on each GPU until the process ends; the pass needs at most 6 KiB of
+ * it for any n (ZERO_ENOSPC otherwise).  Same kernels, grid and results as
+ * zero_shard_unscale_norm_overflow, bit for bit.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race and may return
+ * wrong results.  Nothing needs clearing between calls.  The first call on a
+ * device, with that device current, looks up the array's address there
+ * (no allocation).  Arguments and errors as zero_shard_unscale_norm_overflow,
+ * all checked before the device is touched. */
+int zero_shard_unscale_norm_overflow_noalloc(const void* grad, int32_t grad_dtype, int64_t n,
+                                             double inv_loss_scale, double* d_sqnorm,
+                                             int32_t* d_overflow, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Steps 3+4: fused Adam/AdamW update of one shard and 16-bit writeback.

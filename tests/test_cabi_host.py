@@ -423,3 +423,21 @@ def test_norm_combine_rejects_bad_arguments_on_host():
     assert f(al, al + 64, 8, al + 512, al + 68, None) == L.ZERO_EINVAL
     assert f(al, al + 64, 8, al + 512, al + 516, None) == L.ZERO_EINVAL                   # outputs overlap
 
+
+def test_noalloc_norm_rejects_bad_arguments_on_host():
+    """Every argument is checked before the device is touched (no GPU here)."""
+    lib = L.lib()
+    buf = ctypes.create_string_buffer(256)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    f = lib.zero_shard_unscale_norm_overflow_noalloc
+    assert f(al, L.ZERO_F16, 8, 0.0, al + 64, al + 80, None) == L.ZERO_EINVAL          # inv_loss_scale
+    assert f(al, L.ZERO_F16, 8, float("inf"), al + 64, al + 80, None) == L.ZERO_EINVAL
+    assert f(al, L.ZERO_F16, -1, 1.0, al + 64, al + 80, None) == L.ZERO_EINVAL
+    assert f(al, 7, 8, 1.0, al + 64, al + 80, None) == L.ZERO_EINVAL                   # dtype
+    assert f(al, L.ZERO_F16, 8, 1.0, None, al + 80, None) == L.ZERO_EINVAL
+    assert f(al, L.ZERO_F16, 8, 1.0, al + 64, None, None) == L.ZERO_EINVAL
+    assert f(None, L.ZERO_F16, 8, 1.0, al + 64, al + 80, None) == L.ZERO_EINVAL
+    assert f(al + 2, L.ZERO_F16, 8, 1.0, al + 64, al + 80, None) == L.ZERO_EALIGN
+    assert f(al, L.ZERO_F16, 8, 1.0, al + 68, al + 80, None) == L.ZERO_EALIGN
+    assert f(al, L.ZERO_F16, 8, 1.0, al + 64, al + 82, None) == L.ZERO_EALIGN
+    assert f(al, L.ZERO_F16, 1 << 62, 1.0, al + 64, al + 80, None) == L.ZERO_ERANGE

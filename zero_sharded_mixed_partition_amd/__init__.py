@@ -25,7 +25,8 @@ from ._lib import (ZERO_BF16, ZERO_F16, ZERO_F32, ZeroShardError, zero_adam_hype
                    zero_adam_params, zero_fragment, zero_loss_scaler, zero_step_state)
 
 __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_bytes",
-           "zero_shard_unscale_norm_overflow", "zero_shard_adam_step", "zero_shard_grad_accumulate",
+           "zero_shard_unscale_norm_overflow", "zero_shard_unscale_norm_overflow_noalloc", "zero_shard_adam_step",
+           "zero_shard_grad_accumulate",
            "zero_cpu_shard_unscale_norm_overflow", "zero_cpu_shard_adam_step",
            "zero_loss_scaler_update", "zero_abi_version", "ZERO_F16", "ZERO_BF16", "ZERO_F32",
            "ZeroShardError", "AdamHyper",
@@ -164,6 +165,21 @@ def zero_shard_unscale_norm_overflow(grad, inv_loss_scale: float, sqnorm, overfl
                                                        _typed(overflow, "int32", 1, "overflow"), _ptr(workspace),
                                                        wbytes, _stream(stream)),
              "zero_shard_unscale_norm_overflow")
+
+
+def zero_shard_unscale_norm_overflow_noalloc(grad, inv_loss_scale: float, sqnorm, overflow,
+                                             grad_dtype: Optional[int] = None, n: Optional[int] = None,
+                                             stream=None) -> None:
+    """zero_shard_unscale_norm_overflow with its partials in the library's
+    fixed per-GPU array instead of a workspace: allocates nothing.  Calls
+    that overlap in time on one GPU race (see include/zero_shard.h)."""
+    gd = dtype_code(grad if grad_dtype is None else grad_dtype)
+    n = grad.numel() if n is None else n
+    _L.check(_L.lib().zero_shard_unscale_norm_overflow_noalloc(_grad_ptr(grad, gd, n), gd, n, float(inv_loss_scale),
+                                                               _typed(sqnorm, "float64", 1, "sqnorm"),
+                                                               _typed(overflow, "int32", 1, "overflow"),
+                                                               _stream(stream)),
+             "zero_shard_unscale_norm_overflow_noalloc")
 
 
 class AdamHyper:

@@ -51,6 +51,7 @@ SIGNATURES = {
                                     ctypes.POINTER(zero_fragment), c_i32, P_i32]),
     "zero_norm_workspace_bytes": (c_sz, [c_i64]),
     "zero_shard_unscale_norm_overflow": (c_i32, [c_vp, c_i32, c_i64, c_dbl, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "zero_shard_unscale_norm_overflow_noalloc": (c_i32, [c_vp, c_i32, c_i64, c_dbl, c_vp, c_vp, c_vp]),
     "zero_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                      ctypes.POINTER(zero_adam_params), c_vp, c_vp, c_vp]),
     "zero_shard_grad_accumulate": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_dbl, c_i32, c_vp, c_vp]),

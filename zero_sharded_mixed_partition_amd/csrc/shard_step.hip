@@ -48,6 +48,7 @@
 // graphs.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -881,6 +882,46 @@ size_t zero_norm_workspace_bytes(int64_t n) {
 
 }  // extern "C"
 
+// The norm pass's block partials for zero_shard_unscale_norm_overflow_noalloc:
+// a fixed array in device memory, one copy per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: host code only ever uses the address hipGetSymbolAddress returns for
+// the current device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[8192];
+
+namespace zero_shard {
+namespace {
+
+constexpr size_t kScratchBytes = sizeof(scratch);
+static_assert(((kNormMaxBlocks * (sizeof(double) + sizeof(uint32_t))) + 255) / 256 * 256 <= kScratchBytes,
+              "the norm pass's partials for any n fit the scratch array");
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on each device and kept.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ZERO_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(ZERO_ERANGE, "device %d beyond %d", dev, kMaxScratchDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(ZERO_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zero_shard
+
 namespace zero_shard {
 namespace {
 
@@ -941,6 +982,34 @@ int zero_shard_unscale_norm_overflow(const void* grad, int32_t grad_dtype, int64
         return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
     return norm_pass(grad, grad_dtype, n, inv_loss_scale * inv_loss_scale, nullptr, d_sqnorm, d_overflow,
                      d_workspace, workspace_bytes, static_cast<hipStream_t>(hip_stream));
+}
+
+int zero_shard_unscale_norm_overflow_noalloc(const void* grad, int32_t grad_dtype, int64_t n,
+                                             double inv_loss_scale, double* d_sqnorm, int32_t* d_overflow,
+                                             void* hip_stream) {
+    clear_error();
+    if (!(inv_loss_scale > 0.0) || !std::isfinite(inv_loss_scale))
+        return fail(ZERO_EINVAL, "inv_loss_scale must be finite and > 0");
+    // every argument is checked before the device is touched
+    if (n < 0) return fail(ZERO_EINVAL, "n < 0");
+    if (grad_dtype != ZERO_F16 && grad_dtype != ZERO_BF16 && grad_dtype != ZERO_F32)
+        return fail(ZERO_EINVAL, "unknown grad_dtype %d", grad_dtype);
+    if (d_sqnorm == nullptr || d_overflow == nullptr) return fail(ZERO_EINVAL, "NULL output pointer");
+    if (n > 0 && grad == nullptr) return fail(ZERO_EINVAL, "grad is NULL");
+    if (n > 0 && !aligned16(grad)) return fail(ZERO_EALIGN, "grad must be 16-byte aligned");
+    if (((uintptr_t)d_sqnorm & 7u) || ((uintptr_t)d_overflow & 3u))
+        return fail(ZERO_EALIGN, "d_sqnorm / d_overflow misaligned");
+    if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
+    const size_t need = zero_norm_workspace_bytes(n);
+    if (need > kScratchBytes)
+        return fail(ZERO_ENOSPC, "the norm pass needs %zu bytes of scratch, the fixed array holds %zu", need,
+                    kScratchBytes);
+    void* ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st != ZERO_OK) return st;
+    // the partials kernel writes every slot the combine reads: nothing to clear
+    return norm_pass(grad, grad_dtype, n, inv_loss_scale * inv_loss_scale, nullptr, d_sqnorm, d_overflow, ws,
+                     kScratchBytes, static_cast<hipStream_t>(hip_stream));
 }
 
 int zero_shard_unscale_norm_overflow_dev(const void* grad, int32_t grad_dtype, int64_t n,
