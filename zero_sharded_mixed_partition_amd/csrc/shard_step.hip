@@ -83,23 +83,31 @@ constexpr int kEwTask = 4 * kEwThreads;                         // elements per 
 // never read caps how many such workgroups are resident per CU (160 KiB of
 // LDS per CU on gfx950).  With eight streams in flight HBM sustains more bytes
 // per second when fewer waves compete for DRAM rows.  Chosen by measurement on
-// MI355X, a 976M-element shard stepped as in training (norm pass, update,
-// flag read): 1 task with 12 KiB (13 workgroups per CU) ~81.5% of HBM peak
-// (0 KiB ~75%, 32 KiB ~55%); 4 tasks at 5-6 workgroups per CU ~80%, at 8 or
-// 4 per CU 73-75%; 2 tasks ~79%.  Four tasks would make a skipped step 4x
-// cheaper (every workgroup reads the flag and exits: 0.2 instead of 0.8 ms on
-// that shard), but skipped steps are rare and applied ones are not.
+// MI355X, a 976M-element shard on physically contiguous buffers, all shapes in
+// one process: 1 task with 14 KiB (11 workgroups per CU) 83.5% of HBM peak
+// for a bf16 gradient and 83.2% for an fp32 one, 15 KiB the same, 13 KiB
+// 83.3% / 82.6%, 12 KiB 82.7% / 82.3% (0 KiB ~75%, 32 KiB ~55%); 2 tasks at
+// 18-22 KiB 82.5-82.9% / 80.5-80.9%; 4 tasks at 24-32 KiB 74-82%.  More tasks
+// per workgroup make a skipped step cheaper (every workgroup reads the flag
+// and exits: 0.81, 0.41 and 0.21 ms for 1, 2 and 4 tasks on that shard), but
+// skipped steps are rare and applied ones are not.
 // Task t goes to workgroup t, so consecutive 1 KiB runs of each stream go to
 // the 8 XCDs in turn and the chip streams one narrow window of every buffer.
 // Measured over several processes each on the 976M-element shard: XCDs
 // streaming their own contiguous eighths ~76%, 2 or 4 consecutive tasks per
 // XCD ~80.5% / ~78%, and 512 B tasks (2 elements per lane) ~75-76%, against
 // ~81.7% for this layout.
-constexpr size_t kAdamLdsReserve = 12 * 1024;
+constexpr size_t kAdamLdsReserve = 14 * 1024;
 constexpr int kAdamTasks = 1;
 constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per workgroup
-// The accumulation pass (three streams) is fastest uncapped: 82-84% of HBM
-// peak with no reservation against 45-63% with the 12 KiB cap.
+// The accumulation pass of a later micro-batch (fp32 copy read and written,
+// 16-bit gradient read) is fastest as one task per uncapped one-wave
+// workgroup: 83.8% of HBM peak on a 976M-element shard (2 tasks 78.8-82.1%,
+// 4 tasks 74.6-81.0% over 0-16 KiB caps).  The first micro-batch only writes
+// the copy (2 bytes read, 4 written per element): there two tasks per
+// workgroup, loads first, with a 7 KiB reservation (22 resident per CU) run at
+// 84.1%, the rate of a plain copy reading 8 and writing 16 bytes per lane
+// (84.7%), against 77.3% for one uncapped task; 6 and 8-10 KiB 80.6-83.2%.
 // The reduction and the fused copy-and-norm pass compiled for 5-8 slices
 // (nine or ten streams) gain from a light cap: 6 KiB per one-wave workgroup
 // (26 resident per CU instead of 32) took 8 slices on a 976M-element shard
@@ -107,6 +115,8 @@ constexpr int kAdamGroup = kAdamTasks * kEwTask;                 // elements per
 // 8 KiB and more lose 10-45%.  Capacities 1-4 and 16, and the accumulation
 // kernels, are fastest, or within noise, uncapped.
 constexpr size_t kSlices8Lds = 6 * 1024;
+constexpr int kAccFirstTasks = 2;
+constexpr size_t kAccFirstLds = 7 * 1024;
 constexpr int64_t kEwMaxGrid = (int64_t(1) << 26) - 1;          // grid * 64 work-items < 2^32
 // gfx950 has 8 XCDs, each with its own L2; consecutive workgroups of a launch
 // go to them in turn.  Small per-workgroup results that neighbouring
@@ -538,45 +548,80 @@ __global__ __launch_bounds__(kEwThreads) void adam_update_devcoef(float* __restr
 
 // ---------------------------------------------------------------- gradient accumulation
 
-template <int DT, bool FIRST>
+// T consecutive tasks per one-wave workgroup, all loads issued before any
+// math (straight-line code per task, as in the AdamW pass).
+template <int DT, bool FIRST, int T>
 __global__ __launch_bounds__(kEwThreads) void grad_accumulate(float* __restrict__ A, const void* __restrict__ G,
                                                               int64_t n, float inv,
                                                               const double* __restrict__ d_scale,
                                                               int32_t* __restrict__ d_ovf) {
+    // dynamic LDS reserved by the launcher for the first micro-batch only, to
+    // cap residency; never read
+    extern __shared__ float occupancy_pad[];
     if (d_scale != nullptr) inv = (float)(1.0 / *d_scale);    // device-resident loss scale
     uint32_t bad = 0;
     const int lane = threadIdx.x;
-    const int64_t ntasks = (n + kEwTask - 1) / kEwTask;
-    for (int64_t t = blockIdx.x; t < ntasks; t += gridDim.x) {
-        const int64_t e0 = t * kEwTask + 4 * lane;
-        if (e0 + 4 <= n) {
-            const int64_t q = e0 >> 2;
-            const u32x2 w = ld_stream(static_cast<const u32x2*>(G) + q);
-            bad |= (w[0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
-            bad |= (w[1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
-            float g[4];
-            unpack2<DT>(w[0], g[0], g[1]);
-            unpack2<DT>(w[1], g[2], g[3]);
-            f32x4* a4 = reinterpret_cast<f32x4*>(A) + q;
-            f32x4 a;
-            if constexpr (FIRST) {
+    constexpr int64_t group = (int64_t)T * kEwTask;
+    const int64_t ngroups = (n + group - 1) / group;
+    for (int64_t t = blockIdx.x; t < ngroups; t += gridDim.x) {
+        const int64_t base = t * group;
+        if (base + group <= n) {
+            u32x2 w[T];
+            f32x4 a[T];
+            static_for<T>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int64_t q = (base >> 2) + k * kEwThreads + lane;
+                w[k] = ld_stream(static_cast<const u32x2*>(G) + q);
+                if constexpr (!FIRST) a[k] = ld_stream(reinterpret_cast<f32x4*>(A) + q);
+            });
+            static_for<T>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int64_t q = (base >> 2) + k * kEwThreads + lane;
+                bad |= (w[k][0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                bad |= (w[k][1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                float g[4];
+                unpack2<DT>(w[k][0], g[0], g[1]);
+                unpack2<DT>(w[k][1], g[2], g[3]);
+                f32x4 o;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) a[k] = g[k] * inv;
-            } else {
-                a = ld_stream(a4);
+                for (int j = 0; j < 4; ++j) o[j] = FIRST ? g[j] * inv : fmaf(g[j], inv, a[k][j]);   // one rounding
+                st_stream(o, reinterpret_cast<f32x4*>(A) + q);
+            });
+        } else {
+            // the last, partial group: whole vectors, then the 1-3 element
+            // ragged tail with scalar accesses
+            for (int64_t e0 = base + 4 * lane; e0 < n; e0 += kEwTask) {
+                if (e0 + 4 <= n) {
+                    const int64_t q = e0 >> 2;
+                    const u32x2 w = ld_stream(static_cast<const u32x2*>(G) + q);
+                    bad |= (w[0] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                    bad |= (w[1] & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                    float g[4];
+                    unpack2<DT>(w[0], g[0], g[1]);
+                    unpack2<DT>(w[1], g[2], g[3]);
+                    f32x4* a4 = reinterpret_cast<f32x4*>(A) + q;
+                    f32x4 a;
+                    if constexpr (FIRST) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) a[k] = fmaf(g[k], inv, a[k]);   // one rounding
-            }
-            st_stream(a, a4);
-        } else if (e0 < n) {
-            for (int64_t e = e0; e < n; ++e) {
-                const uint32_t h = static_cast<const uint16_t*>(G)[e];
-                bad |= (h & GradFmt<DT>::mask) + GradFmt<DT>::carry;
-                const float g = load_grad1<DT>(G, e);
-                A[e] = FIRST ? g * inv : fmaf(g, inv, A[e]);
+                        for (int k = 0; k < 4; ++k) a[k] = g[k] * inv;
+                    } else {
+                        a = ld_stream(a4);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) a[k] = fmaf(g[k], inv, a[k]);
+                    }
+                    st_stream(a, a4);
+                } else {
+                    for (int64_t e = e0; e < n; ++e) {
+                        const uint32_t h = static_cast<const uint16_t*>(G)[e];
+                        bad |= (h & GradFmt<DT>::mask) + GradFmt<DT>::carry;
+                        const float g = load_grad1<DT>(G, e);
+                        A[e] = FIRST ? g * inv : fmaf(g, inv, A[e]);
+                    }
+                }
             }
         }
     }
+    if (n < 0) occupancy_pad[lane] = 0.0f;   // never taken (n >= 0): keeps the reservation referenced
     if (d_ovf != nullptr && (bad & kNonfiniteBits) != 0) atomicOr(d_ovf, 1);
 }
 
@@ -1180,17 +1225,21 @@ int accumulate(float* acc, const void* grad, int32_t grad_dtype, int64_t n, doub
     if (n > INT64_MAX / 4) return fail(ZERO_ERANGE, "n too large");
     if (overlaps(acc, n * 4, grad, n * 2)) return fail(ZERO_EINVAL, "acc aliases grad");
     if (d_overflow && overlaps(acc, n * 4, d_overflow, sizeof(int32_t))) return fail(ZERO_EINVAL, "d_overflow lies in acc");
-    const dim3 grid = elementwise_grid(n);
     const float inv = (float)inv_loss_scale;
-#define ZS_ACC(DT, F) hipLaunchKernelGGL((grad_accumulate<DT, F>), grid, dim3(kEwThreads), 0, s, acc, grad, n, inv, \
-                                         d_scale, d_overflow)
-    if (grad_dtype == ZERO_F16) {
-        if (first) ZS_ACC(ZERO_F16, true);
-        else ZS_ACC(ZERO_F16, false);
-    } else {
-        if (first) ZS_ACC(ZERO_BF16, true);
-        else ZS_ACC(ZERO_BF16, false);
-    }
+    // the first micro-batch: kAccFirstTasks tasks per workgroup, capped
+    // residency; later ones: one task per uncapped workgroup
+    const dim3 grid = elementwise_grid(n, first ? (int64_t)kAccFirstTasks * kEwTask : kEwTask);
+#define ZS_ACC(DT)                                                                                             \
+    do {                                                                                                       \
+        if (first)                                                                                             \
+            hipLaunchKernelGGL((grad_accumulate<DT, true, kAccFirstTasks>), grid, dim3(kEwThreads),            \
+                               kAccFirstLds, s, acc, grad, n, inv, d_scale, d_overflow);                       \
+        else                                                                                                   \
+            hipLaunchKernelGGL((grad_accumulate<DT, false, 1>), grid, dim3(kEwThreads), 0, s, acc, grad, n,    \
+                               inv, d_scale, d_overflow);                                                      \
+    } while (0)
+    if (grad_dtype == ZERO_F16) ZS_ACC(ZERO_F16);
+    else ZS_ACC(ZERO_BF16);
 #undef ZS_ACC
     return launch_status("grad_accumulate");
 }
