@@ -4,12 +4,15 @@ The elementwise passes launch at most 2^26 - 1 one-wave workgroups (grid
 size times 64 work-items must stay below 2^32), 256 elements each; past
 2^34 elements they stride over the remaining tasks.  This shard has
 2^34 + 4099 elements (ragged), so the last tasks, and the tail, go through
-that stride.  The fp32 accumulation copy (69 GB) and one bf16 gradient
+that stride.  (The first micro-batch's accumulation takes two tasks, 512
+elements, per workgroup: its grid covers this shard in one launch, and the
+partial last group takes its per-lane path.  A later micro-batch's strides.)  The fp32 accumulation copy (69 GB) and one bf16 gradient
 (34 GB) fit in one MI355X's HBM; the update's 16 B/element would not.
 
 The gradient repeats a table of 251 bf16 values (g_i = T[i mod 251]), filled
 on the device, so every expected value is known in closed form:
   * accumulate (first):       acc_i = T[i mod 251]
+  * accumulate (later):       acc_i = 2 T[i mod 251]
   * reduce of two slices:     acc_i = 2 T[i mod 251]   (both slices the same buffer)
   * fused add + norm:         acc_i = 3 T[i mod 251], sum of squares
                               = 9 sum_r count_r T_r^2, formed exactly with
@@ -81,6 +84,11 @@ def test_passes_beyond_one_grid(Z):
         torch.cuda.synchronize()
         assert int(flag.item()) == 0
         _check(A, T64, 1, "accumulate")
+
+        Z.zero_shard_grad_accumulate(A, G, 1.0, first=False, overflow=flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        _check(A, T64, 2, "accumulate, later micro-batch")
 
         Z.zero_shard_grad_reduce(A, [G, G], 1.0, overflow=flag)
         torch.cuda.synchronize()
