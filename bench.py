@@ -426,7 +426,11 @@ def run_shard(w, args, K, R, steps, warmup):
             for k in range(K):
                 if ev is not None and k == K - 1:
                     ev[3].record()
+                if ev is not None and k == 0 and K > 1:
+                    ev[7].record()
                 opt.accumulate(A, G, first=(k == 0), last=FUSED and k == K - 1)
+                if ev is not None and k == 0 and K > 1:
+                    ev[8].record()
             if ev is not None:
                 ev[4].record()
         if R:
@@ -461,7 +465,7 @@ def run_shard(w, args, K, R, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(steps)]
     skipped = 0
     wall = []
     skipped0 = opt.read_state().skipped if DS else 0
@@ -499,7 +503,7 @@ def run_shard(w, args, K, R, steps, warmup):
     n_skip = min(10, steps)
     keep = G[S // 2].clone()
     G[S // 2] = float("inf")
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_skip)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(n_skip)]
     skipped1 = opt.read_state().skipped if DS else 0
     torch.cuda.synchronize()
     skip_wall = []
@@ -540,6 +544,25 @@ def run_shard(w, args, K, R, steps, warmup):
                        "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
                        "gbps": (ACC_BYTES_PER_PARAM if K > 1 else ACC_FIRST_BYTES_PER_PARAM) * S / (acc_ms * 1e-3) / 1e9,
                        "traffic": measured_traffic(run_key, "grad_sum_norm" if FUSED else "grad_accumulate")}
+        if K > 1:
+            # the first micro-batch (2 B read, 4 B written per element) against
+            # the widening copy over the same bytes: G (2 B/param) into A (4 B/param)
+            first_ms = mean([e[7].elapsed_time(e[8]) for e in evs])
+            first_gbps = ACC_FIRST_BYTES_PER_PARAM * S / (first_ms * 1e-3) / 1e9
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for _ in range(3):
+                Z.zero_copy_widen_reference(A, G, 2 * S)
+            c0.record()
+            for _ in range(10):
+                Z.zero_copy_widen_reference(A, G, 2 * S)
+            c1.record()
+            torch.cuda.synchronize()
+            widen_gbps = ACC_FIRST_BYTES_PER_PARAM * S / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+            accum_stats["first"] = {"kernel": "grad_accumulate (first micro-batch)", "avg_ms": first_ms,
+                                    "algorithmic_bytes": ACC_FIRST_BYTES_PER_PARAM * S, "gbps": first_gbps,
+                                    "frac_of_peak": first_gbps / PEAK_HBM_GBPS,
+                                    "traffic": measured_traffic(run_key, "grad_accumulate_first"),
+                                    "widening_copy_gbps": widen_gbps, "frac_of_widening_copy": first_gbps / widen_gbps}
     reduce_stats = None
     if R:
         red_ms = mean([e[3].elapsed_time(e[4]) for e in evs])

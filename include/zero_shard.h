@@ -538,6 +538,15 @@ int zero_shard_grad_sum_norm_dev(float* acc, const void* const* slices, int32_t 
  * ------------------------------------------------------------------------- */
 int zero_copy_reference(void* dst, const void* src, int64_t bytes, void* hip_stream);
 
+/* Extra, a measurement aid: the widening copy.  Reads src_bytes (a multiple
+ * of 8) and writes 2 * src_bytes: each 8-byte word of src lands twice, as one
+ * 16-byte vector of dst.  8 bytes read and 16 written per lane, the access
+ * pattern of the first micro-batch's accumulation (2 bytes read, 4 written
+ * per element), whose achievable rate it measures.  dst, src: device,
+ * 16-byte aligned, not overlapping; async on hip_stream.
+ * Errors: ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE, ZERO_EHIP. */
+int zero_copy_widen_reference(void* dst, const void* src, int64_t src_bytes, void* hip_stream);
+
 /* ---------------------------------------------------------------------------
  * The local half of the all-reduce of the norm pass's two scalars: the one
  * exchange inside the step (extra: a row around the step).  Each rank

@@ -235,6 +235,14 @@ def test_copy_reference_rejects_bad_arguments_on_host():
     assert cp(al + 8, al + 64, 16, None) == L.ZERO_EALIGN
     assert cp(al, al + 16, 32, None) == L.ZERO_EINVAL               # overlapping
     assert cp(al, al + 64, 1 << 60, None) == L.ZERO_EINVAL           # overlapping (any size is accepted)
+    wc = lib.zero_copy_widen_reference
+    assert wc(al, al + 128, 0, None) == L.ZERO_OK                   # empty: nothing launched
+    assert wc(al, al + 128, 12, None) == L.ZERO_EINVAL              # not a multiple of 8
+    assert wc(al, al + 128, -8, None) == L.ZERO_EINVAL
+    assert wc(None, al, 8, None) == L.ZERO_EINVAL
+    assert wc(al + 8, al + 128, 8, None) == L.ZERO_EALIGN
+    assert wc(al, al + 16, 16, None) == L.ZERO_EINVAL               # dst [al, al+32) overlaps src [al+16, al+32)
+    assert wc(al, al + 64, 1 << 62, None) == L.ZERO_ERANGE          # 2 * src_bytes overflows
 
 
 def test_reduce_rejects_bad_arguments_on_host():

@@ -40,6 +40,9 @@ def test_bench_json_line(extra):
         assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == "params/s"
     if "--reduce" in extra:
         assert d["reduce"]["slices"] == 3 and d["reduce"]["gbps"] > 0
+    if "--accum" in extra:
+        f = d["accumulate"]["first"]
+        assert f["gbps"] > 0 and f["widening_copy_gbps"] > 0 and abs(f["frac_of_widening_copy"] - f["gbps"] / f["widening_copy_gbps"]) < 1e-12
     # the shard's buffers come from the library's contiguous pool; the label
     # says whether any segment fell back to ordinary memory
     assert d["config"]["buffers"].startswith("physically contiguous HBM") and "none fell back" in d["config"]["buffers"]

@@ -32,6 +32,7 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "ZeroShardError", "AdamHyper",
            "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam", "StepGraph", "zero_adam_coef_bytes",
            "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
+           "zero_copy_widen_reference",
            "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
            "zero_shard_norm_decide_dev", "StepGraphDev", "zero_sum_norm_workspace_bytes", "zero_shard_grad_sum_norm",
@@ -401,6 +402,14 @@ def zero_copy_reference(dst, src, nbytes: Optional[int] = None, stream=None) -> 
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _L.check(_L.lib().zero_copy_reference(_dev(dst, int(nbytes), "dst"), _dev(src, int(nbytes), "src"), int(nbytes),
                                           _stream(stream)), "zero_copy_reference")
+
+
+def zero_copy_widen_reference(dst, src, src_bytes: Optional[int] = None, stream=None) -> None:
+    """Widening device copy: reads src_bytes (default: all of src), writes
+    twice that to dst (8 bytes read, 16 written per lane)."""
+    src_bytes = src.numel() * src.element_size() if src_bytes is None else src_bytes
+    _L.check(_L.lib().zero_copy_widen_reference(_dev(dst, 2 * int(src_bytes), "dst"), _dev(src, int(src_bytes), "src"),
+                                                int(src_bytes), _stream(stream)), "zero_copy_widen_reference")
 
 
 class StepState:

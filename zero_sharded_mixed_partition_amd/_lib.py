@@ -78,6 +78,7 @@ SIGNATURES = {
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
     "zero_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
+    "zero_copy_widen_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "zero_device_alloc_contiguous": (c_i32, [ctypes.POINTER(c_vp), c_sz]),
     "zero_device_free": (c_i32, [c_vp]),
     "zero_pool_alloc": (c_vp, [c_sz, c_i32, c_vp]),
