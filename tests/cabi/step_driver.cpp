@@ -10,6 +10,8 @@
 //     fp32 master, bit for bit;
 //   * an inf anywhere sets the flag and the step writes nothing;
 //   * the step with the loss scaler in device memory gives the same bits;
+//   * the norm pass without a workspace (its partials in the library's fixed
+//     array) gives the same bits, and flags the inf;
 //   * a misaligned pointer is rejected with ZERO_EALIGN and a detail string.
 // Prints "ok" and exits 0 on success; anything else is a failure.
 #include <hip/hip_runtime_api.h>
@@ -213,6 +215,23 @@ int main() {
         CHECK(std::memcmp(p3.data(), p1.data(), n * 4) == 0 && std::memcmp(m3.data(), m1.data(), n * 4) == 0 &&
                   std::memcmp(v3.data(), v1.data(), n * 4) == 0 && std::memcmp(par3.data(), par1.data(), n * 2) == 0,
               "the device-state step differs from the host-scaled one");
+    }
+
+    // the norm pass that allocates nothing and takes no workspace: the closed
+    // form on the finite gradient, the flag and +inf on the one holding an inf
+    for (int rep = 0; rep < 2; ++rep) {
+        st = zero_shard_unscale_norm_overflow_noalloc(b.G, ZERO_BF16, n, 1.0, d_sq, d_ovf, stream);
+        CHECK(st == ZERO_OK, "norm pass without a workspace: %s", zero_last_error());
+        HIP_OK(hipStreamSynchronize(stream));
+        HIP_OK(hipMemcpy(&sq, d_sq, sizeof(sq), hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&ovf, d_ovf, sizeof(ovf), hipMemcpyDeviceToHost));
+        CHECK(ovf == 0 && sq == sq_ref, "no-workspace norm %.17g (flag %d), closed form %.17g", sq, ovf, sq_ref);
+        st = zero_shard_unscale_norm_overflow_noalloc(a.G, ZERO_BF16, n, 1.0, d_sq, d_ovf, stream);
+        CHECK(st == ZERO_OK, "norm pass without a workspace: %s", zero_last_error());
+        HIP_OK(hipStreamSynchronize(stream));
+        HIP_OK(hipMemcpy(&sq, d_sq, sizeof(sq), hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(&ovf, d_ovf, sizeof(ovf), hipMemcpyDeviceToHost));
+        CHECK(ovf == 1 && std::isinf(sq) && sq > 0, "no-workspace norm with an inf: %.17g (flag %d)", sq, ovf);
     }
 
     // errors are reported, not launched: a master pointer off by 4 bytes
