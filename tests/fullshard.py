@@ -100,24 +100,27 @@ def _examples(bad, got, ref, lo: int):
 
 def tally_f32(t: Tally, got, ref, lo: int, rel: float = REL, abs_: float = ABS):
     """|got - ref| <= max(rel * |ref|, abs_) for float32 tensors (either
-    device); worst = max |got - ref| / |ref|.  NaN on either side is outside."""
+    device); worst = the largest |got - ref| as a fraction of what the bar
+    allows there (at most 1 when all pass).  NaN on either side is outside."""
     import torch
     g, r = got.double(), ref.double()
     err = (g - r).abs()
-    bad = ~(err <= torch.clamp(r.abs() * rel, min=abs_))
+    tol = torch.clamp(r.abs() * rel, min=abs_)
+    bad = ~(err <= tol)
     nbad = int(bad.sum())
-    worst = float((err / torch.clamp(r.abs(), min=1e-30)).max()) if err.numel() else 0.0
+    worst = float((err / tol).nan_to_num(float("inf")).max()) if err.numel() else 0.0
     t.add(err.numel(), nbad, worst, _examples(bad, got, ref, lo) if nbad else [])
 
 
 def tally_strict_v(t: Tally, got, ref, lo: int):
-    """Second moment: |got - ref| <= 1e-6 * |ref| + 1e-40 (parity.strict_v)."""
-    import torch
+    """Second moment: |got - ref| <= 1e-6 * |ref| + 1e-40 (parity.strict_v);
+    worst as in tally_f32."""
     g, r = got.double(), ref.double()
     err = (g - r).abs()
-    bad = ~(err <= r.abs() * 1e-6 + 1e-40)
+    tol = r.abs() * 1e-6 + 1e-40
+    bad = ~(err <= tol)
     nbad = int(bad.sum())
-    worst = float((err / torch.clamp(r, min=1e-38)).max()) if err.numel() else 0.0
+    worst = float((err / tol).nan_to_num(float("inf")).max()) if err.numel() else 0.0
     t.add(err.numel(), nbad, worst, _examples(bad, got, ref, lo) if nbad else [])
 
 
@@ -177,6 +180,9 @@ def tally_ulp_f32(t: Tally, got, ref, lo: int):
 
 
 def assert_all(tallies):
+    """Every tally clean and non-empty; tallies whose name says "report only" are
+    left out of the check."""
+    tallies = [t for t in tallies if "report only" not in t.name]
     bad = [t for t in tallies if not t.ok()]
     assert not bad, "; ".join(repr(t) for t in bad)
     for t in tallies:

@@ -44,6 +44,13 @@ def test_tally_f32_matches_parity_check():
     ok = F.Tally("ok")
     F.tally_f32(ok, torch.from_numpy(ref), torch.from_numpy(ref), 0)
     F.assert_all([ok])
+    assert ok.worst == 0.0 and t.worst > 1.0                   # a fraction of the allowed error
+    half = F.Tally("half")
+    r1 = np.array([1.0, 1e-9], np.float32)
+    g1 = np.array([1.0 + 0.5e-5, 1e-9 + 0.25e-7], np.float32)
+    F.tally_f32(half, torch.from_numpy(g1), torch.from_numpy(r1), 0)
+    assert half.ok() and 0.45 < half.worst < 0.51             # float32 rounding of the planted values
+    F.assert_all([half, F.Tally("skipped (report only)")])
 
 
 def test_tally_strict_v_matches_parity():

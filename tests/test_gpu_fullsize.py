@@ -83,16 +83,15 @@ def _compare(blocks, got, ref, what, pfmt, strict=True):
     returns the tallies (all must be clean)."""
     P, M, V, par = got
     RP, RM, RV, RPAR = ref
-    names = ["master", "exp_avg", "exp_avg_sq"] + (["exp_avg_sq (strict)"] if strict else []) + \
-        ["param", "param = RNE(own master)"]
+    vs = "exp_avg_sq (strict)" if strict else "exp_avg_sq (strict, report only)"
+    names = ["master", "exp_avg", "exp_avg_sq", vs, "param", "param = RNE(own master)"]
     tl = {k: F.Tally(what + k) for k in names}
     pb, rb = par.view(torch.int16), RPAR.view(torch.int16)
     for lo, hi in blocks:
         F.tally_f32(tl["master"], P[lo:hi], RP[lo:hi], lo)
         F.tally_f32(tl["exp_avg"], M[lo:hi], RM[lo:hi], lo)
         F.tally_f32(tl["exp_avg_sq"], V[lo:hi], RV[lo:hi], lo)
-        if strict:
-            F.tally_strict_v(tl["exp_avg_sq (strict)"], V[lo:hi], RV[lo:hi], lo)
+        F.tally_strict_v(tl[vs], V[lo:hi], RV[lo:hi], lo)
         F.tally_param(tl["param"], pb[lo:hi], rb[lo:hi], lo, pfmt)
         F.tally_writeback(tl["param = RNE(own master)"], P[lo:hi], pb[lo:hi], lo, pfmt)
     tl = list(tl.values())
