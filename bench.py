@@ -13,7 +13,9 @@ Inputs are seeded synthetic values uploaded to HBM before timing.
 
 Prints one JSON line.  `value` is params/s of the whole step; `roofline`
 reports the fused AdamW kernel (the dominant one) against MI355X's 8 TB/s HBM
-peak, from HIP events recorded on the stream it runs on.
+peak, from HIP events recorded on the stream it runs on.  On the default
+path the 100B model's 250M-parameter rank shard is timed afterwards the same
+way and reported under `extra_workload`; `value` stays the first shard's.
 """
 import argparse
 import contextlib
