@@ -214,6 +214,38 @@ def bench_offload(w, args):
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     avg = {k: sum(v) / len(v) * 1e3 for k, v in phases.items()}
     pcie_bytes = 2 * S
+
+    # host ceilings, after the timed region: the host step alone over the
+    # whole shard (no PCIe; 2 + 12 bytes read, 12 + 2 written per parameter)
+    # and the library's host copy of the master's bytes (the step's chunks,
+    # threads and store style: one read and one write stream)
+    g_host = torch.empty(S, dtype=tdt[w.grad_dtype], pin_memory=True)
+    g_host.copy_(G)
+    p_host = torch.empty(S, dtype=tdt[w.param_dtype], pin_memory=True)
+    sq_h, _ = Z.zero_cpu_shard_unscale_norm_overflow(g_host, 1.0 / opt.scaler.scale)
+    hp_h = Z.AdamHyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                       step=opt.t + 1, inv_loss_scale=1.0 / opt.scaler.scale, max_grad_norm=w.max_grad_norm)
+    host_ms = []
+    for _ in range(3):
+        h0 = time.perf_counter()
+        Z.zero_cpu_shard_adam_step(host[0], host[1], host[2], g_host, p_host, hp_h, sq_h, False)
+        host_ms.append((time.perf_counter() - h0) * 1e3)
+    scratch = torch.empty_like(host[0])
+    copy_ms = []
+    for _ in range(3):
+        h0 = time.perf_counter()
+        Z.zero_cpu_copy_reference(scratch, host[0])
+        copy_ms.append((time.perf_counter() - h0) * 1e3)
+    host_step_ms, host_copy_ms = min(host_ms), min(copy_ms)
+    # plain stores to a line not yet in a cache read it first (write-allocate):
+    # the copy moves 4 + 4 + 4 bytes per float, the step 28 + 2 per parameter
+    # (its fp32 streams are updated in place; only the 16-bit copy is
+    # write-allocated)
+    host_step_gbps = 28 * S / (host_step_ms * 1e-3) / 1e9
+    host_copy_gbps = 8 * S / (host_copy_ms * 1e-3) / 1e9
+    host_step_wa = 30 * S / (host_step_ms * 1e-3) / 1e9
+    host_copy_wa = 12 * S / (host_copy_ms * 1e-3) / 1e9
+    del g_host, p_host, scratch
     out = {
         "metric": METRIC, "value": S / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -222,7 +254,13 @@ def bench_offload(w, args):
                    "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "host_threads": os.cpu_count()},
         "offload": {"phase_ms": avg, "chunk": opt.chunk, "norm_on": "device",
                     "pcie_gbps_each_way": pcie_bytes / (avg["pipeline"] * 1e-3) / 1e9,
-                    "host_state_gbps": 24 * S / (avg["pipeline"] * 1e-3) / 1e9},
+                    "host_state_gbps": 24 * S / (avg["pipeline"] * 1e-3) / 1e9,
+                    "host_step_alone": {"ms": host_step_ms, "gbps": host_step_gbps, "bytes_per_param": 28,
+                                        "gbps_with_write_allocate": host_step_wa, "threads": os.cpu_count()},
+                    "host_copy": {"ms": host_copy_ms, "gbps": host_copy_gbps, "gbps_with_write_allocate": host_copy_wa,
+                                  "what": "zero_cpu_copy_reference over the fp32 master's bytes: one read and one "
+                                          "write stream on the host step's threads"},
+                    "host_step_frac_of_copy": host_step_wa / host_copy_wa},
         "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

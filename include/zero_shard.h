@@ -373,6 +373,14 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
                              const zero_adam_params* hp, double global_sqnorm,
                              int32_t global_overflow, int32_t nthreads);
 
+/* Extra, a measurement aid for the host step: a plain copy of `bytes` (a
+ * multiple of 4) from src to dst in host memory, cut into the same chunks and
+ * run on the same worker threads, with the same vectorized store style as the
+ * host AdamW loop: the achievable rate of one read and one write stream on
+ * the host cores.  Synchronous; host pointers, not overlapping; nthreads as
+ * above.  Errors: ZERO_EINVAL. */
+int zero_cpu_copy_reference(void* dst, const void* src, int64_t bytes, int32_t nthreads);
+
 /* ---------------------------------------------------------------------------
  * Step 2 (scalar, host): dynamic loss scale update after a step.  Contract
  * call.  Passage: the pages name mixed-precision (fp16) training

@@ -154,3 +154,27 @@ def test_cpu_step_huge_unclipped_gradients(gfmt):
     ref = oracle.shard_step(p, m, v, g, gfmt, "bf16", global_sq=ref_sq, global_overflow=False, **hp)
     assert np.isfinite(V).all()
     compare_step((P, M, V, par), ref)
+
+
+@pytest.mark.parametrize("nbytes", [0, 4, 12, (1 << 18) - 4, (1 << 18) + 4, 3 * (1 << 20) + 8])
+@pytest.mark.parametrize("threads", [1, 3, 0])
+def test_host_copy_reference(nbytes, threads):
+    """The host copy moves every byte and nothing beyond its range, for any
+    thread count (chunks of 2^16 floats)."""
+    rng = np.random.default_rng(nbytes + threads)
+    src = rng.integers(0, 2**32, size=nbytes // 4 + 8, dtype=np.uint64).astype(np.uint32)
+    dst = np.zeros_like(src)
+    Z.zero_cpu_copy_reference(dst, src, nbytes, nthreads=threads)
+    n = nbytes // 4
+    assert (dst[:n] == src[:n]).all() and not dst[n:].any()
+
+
+def test_host_copy_reference_rejects_bad_arguments():
+    lib = Z._L.lib()
+    a = np.zeros(64, np.uint32)
+    p = a.ctypes.data
+    assert lib.zero_cpu_copy_reference(p, p + 128, 6, 0) == Z._L.ZERO_EINVAL          # not a multiple of 4
+    assert lib.zero_cpu_copy_reference(p, p + 128, -4, 0) == Z._L.ZERO_EINVAL
+    assert lib.zero_cpu_copy_reference(None, p, 4, 0) == Z._L.ZERO_EINVAL
+    assert lib.zero_cpu_copy_reference(p, p + 16, 32, 0) == Z._L.ZERO_EINVAL          # overlapping
+    assert lib.zero_cpu_copy_reference(p, p + 128, 0, 0) == Z._L.ZERO_OK

@@ -32,7 +32,7 @@ __all__ = ["zero_partition_plan", "zero_rank_fragments", "zero_norm_workspace_by
            "ZeroShardError", "AdamHyper",
            "LossScaler", "dtype_code", "ShardAdam", "OffloadShardAdam", "StepGraph", "zero_adam_coef_bytes",
            "zero_adam_prepare", "zero_shard_adam_step_coef", "zero_shard_grad_reduce", "zero_copy_reference",
-           "zero_copy_widen_reference",
+           "zero_copy_widen_reference", "zero_cpu_copy_reference",
            "MAX_SLICES", "StepState", "zero_shard_unscale_norm_overflow_dev", "zero_shard_adam_step_dev",
            "zero_shard_grad_accumulate_dev", "zero_shard_grad_reduce_dev", "zero_step_decide_dev",
            "zero_shard_norm_decide_dev", "StepGraphDev", "zero_sum_norm_workspace_bytes", "zero_shard_grad_sum_norm",
@@ -289,6 +289,17 @@ def zero_cpu_shard_unscale_norm_overflow(grad, inv_loss_scale: float, grad_dtype
                                                            ctypes.byref(sq), ctypes.byref(ovf), int(nthreads)),
              "zero_cpu_shard_unscale_norm_overflow")
     return sq.value, bool(ovf.value)
+
+
+def zero_cpu_copy_reference(dst, src, nbytes: Optional[int] = None, nthreads: int = 0) -> None:
+    """Host-memory copy in the host step's chunks, threads and store style
+    (synchronous): the host cores' one-read-one-write streaming rate."""
+    size = lambda a: a.nbytes if hasattr(a, "ctypes") else a.numel() * a.element_size()  # noqa: E731
+    nbytes = size(src) if nbytes is None else int(nbytes)
+    if size(dst) < nbytes or size(src) < nbytes:
+        raise ValueError(f"buffers hold {size(dst)} / {size(src)} bytes, the copy moves {nbytes}")
+    _L.check(_L.lib().zero_cpu_copy_reference(_host_ptr(dst), _host_ptr(src), nbytes, int(nthreads)),
+             "zero_cpu_copy_reference")
 
 
 def zero_cpu_shard_adam_step(master, exp_avg, exp_avg_sq, grad, param_out, hp: AdamHyper, global_sqnorm: float,

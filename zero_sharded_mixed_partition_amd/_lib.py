@@ -76,6 +76,7 @@ SIGNATURES = {
     "zero_cpu_shard_unscale_norm_overflow": (c_i32, [c_vp, c_i32, c_i64, c_dbl, ctypes.POINTER(c_dbl), P_i32, c_i32]),
     "zero_cpu_shard_adam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                          ctypes.POINTER(zero_adam_params), c_dbl, c_i32, c_i32]),
+    "zero_cpu_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_i32]),
     "zero_loss_scaler_update": (c_i32, [ctypes.POINTER(zero_loss_scaler), c_i32, P_i32]),
     "zero_copy_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "zero_copy_widen_reference": (c_i32, [c_vp, c_vp, c_i64, c_vp]),

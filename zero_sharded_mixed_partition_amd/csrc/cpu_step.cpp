@@ -170,6 +170,11 @@ ZS_CLONES void adam_f32(float* __restrict p, float* __restrict m, float* __restr
     }
 }
 
+// dst = src over n floats, in the same vectorized store style as adam_f32
+ZS_CLONES void copy_f32(float* __restrict dst, const float* __restrict src, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------- threading
 
 int resolve_threads(int32_t nthreads, int64_t nchunks) {
@@ -377,6 +382,21 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
                 else encode_bf16(master + e, po, cnt);
             }
         }
+    });
+    return ZERO_OK;
+}
+
+int zero_cpu_copy_reference(void* dst, const void* src, int64_t bytes, int32_t nthreads) {
+    clear_error();
+    if (bytes < 0 || (bytes & 3)) return fail(ZERO_EINVAL, "bytes must be a non-negative multiple of 4");
+    if (bytes == 0) return ZERO_OK;
+    if (dst == nullptr || src == nullptr) return fail(ZERO_EINVAL, "NULL pointer");
+    if (overlaps(dst, bytes, src, bytes)) return fail(ZERO_EINVAL, "dst and src overlap");
+    const int64_t n = bytes / 4;
+    const int64_t nchunks = (n + kChunk - 1) / kChunk;
+    for_chunks(nchunks, resolve_threads(nthreads, nchunks), [&](int64_t ch) {
+        const int64_t lo = ch * kChunk, hi = lo + kChunk < n ? lo + kChunk : n;
+        copy_f32(static_cast<float*>(dst) + lo, static_cast<const float*>(src) + lo, hi - lo);
     });
     return ZERO_OK;
 }
