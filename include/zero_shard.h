@@ -37,7 +37,9 @@
  *    ranks' scalars, and the step on host cores (whose worker threads start
  *    on first use and live until the process ends);
  *  - physically contiguous memory (zero_device_alloc_contiguous, zero_pool_*),
- *    whose purpose is to allocate, and the measurement copy.
+ *    whose purpose is to allocate, and the measurement copies
+ *    (zero_copy_reference, zero_copy_widen_reference on the device,
+ *    zero_cpu_copy_reference on the host).
  *
  * Conventions for every function:
  *  - Returns an int status: ZERO_OK (0) or a negative zero_status (the
