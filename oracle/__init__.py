@@ -34,7 +34,8 @@ and by torch.optim.AdamW on the CPU, not by the pages ("parity unpinned" by the
 pages for the update formula; pinned by the textbook method).
 """
 from .plan import partition_plan, rank_fragments, rank_range  # noqa: F401
-from .accounting import model_state_bytes_per_param, per_rank_state_bytes, reduction_factor  # noqa: F401
+from .accounting import (model_state_bytes_per_param, per_rank_state_bytes, reduction_factor,  # noqa: F401
+                         communication_elements)
 from .formats import decode16, is_nonfinite16, encode16_rne  # noqa: F401
 from .adam import (shard_sqnorm_overflow, global_sqnorm_overflow, sqnorm_terms,  # noqa: F401
                    combine_sqnorm_terms, SqnormTerms, clip_coefficient, grad_scale, adam_update,

@@ -17,6 +17,20 @@ Per-rank bytes by stage, Psi parameters over N_d ranks:
   P_os             4 Psi + 12 Psi / N_d    (optimizer states sharded)
   P_os+g           2 Psi + 14 Psi / N_d    (+ gradients)
   P_os+g+p         16 Psi / N_d            (+ parameters)
+
+Communication per training step ([Explainer, Ch.02 "The Three Stages", what
+each stage shards; Ch.05 stage table, extra-communication column]): baseline
+DP all-reduces the gradient; the first two stages move about the same volume;
+the third moves half as much again, gathering parameters and reduce-scattering
+gradients.  Reading: ring collectives, in which a reduce-scatter or an
+all-gather of a Psi-element buffer has every rank send (N_d - 1) / N_d * Psi
+elements and an all-reduce is the two in turn.  DP: one all-reduce of the
+gradient (2 units).  P_os and P_os+g: a reduce-scatter of the gradient, so
+each rank holds the reduced gradient of its partition, then an all-gather of
+the updated parameters (2 units).  P_os+g+p: each rank keeps only its
+partition of the parameters, so they are all-gathered before the forward pass
+and again before the backward pass, and the gradient is reduce-scattered
+after it (3 units, half as much again as DP).
 """
 from fractions import Fraction
 
@@ -49,3 +63,15 @@ def per_rank_state_bytes(stage: str, psi: int, n_d: int) -> Fraction:
 def reduction_factor(stage: str, psi: int, n_d: int) -> Fraction:
     """Per-rank memory of baseline DP divided by that of `stage`."""
     return per_rank_state_bytes("dp", psi, n_d) / per_rank_state_bytes(stage, psi, n_d)
+
+
+COLLECTIVES_PER_STEP = {"dp": 2, "os": 2, "os+g": 2, "os+g+p": 3}   # reduce-scatter / all-gather units
+
+
+def communication_elements(stage: str, psi: int, n_d: int) -> Fraction:
+    """Elements one rank sends per training step (ring collectives)."""
+    if stage not in STAGES:
+        raise ValueError(stage)
+    if n_d < 1:
+        raise ValueError("n_d >= 1")
+    return COLLECTIVES_PER_STEP[stage] * Fraction((n_d - 1) * psi, n_d)

@@ -6,7 +6,7 @@ from fractions import Fraction
 
 import pytest
 
-from oracle import model_state_bytes_per_param, per_rank_state_bytes, reduction_factor
+from oracle import communication_elements, model_state_bytes_per_param, per_rank_state_bytes, reduction_factor
 from oracle import accounting as A
 
 
@@ -64,3 +64,19 @@ def test_exact_per_rank_formulas():
     assert per_rank_state_bytes("os", psi, n_d) == 4 * psi + Fraction(12 * psi, n_d)
     assert per_rank_state_bytes("os+g", psi, n_d) == 2 * psi + Fraction(14 * psi, n_d)
     assert per_rank_state_bytes("os+g+p", psi, n_d) == Fraction(16 * psi, n_d)
+
+
+def test_stage_communication(facts):
+    """The stage table's extra communication: none for the first two stages,
+    half as much again as plain DP for the third, at any N_d >= 2."""
+    psi = 7 * 10**9
+    for n_d in (2, 8, 400, 1024):
+        dp = communication_elements("dp", psi, n_d)
+        for stage, fid in (("os", "extra_comm_zero1_pos"), ("os+g", "extra_comm_zero2_posg"),
+                           ("os+g+p", "extra_comm_zero3_posgp")):
+            extra = communication_elements(stage, psi, n_d) / dp - 1
+            assert extra == Fraction(facts[fid]["approx_extra_fraction"]).limit_denominator(100)
+    # one rank alone sends nothing; a ring all-reduce sends 2 (N_d - 1) / N_d of the buffer
+    assert communication_elements("dp", psi, 1) == 0
+    assert communication_elements("dp", 1000, 4) == 1500
+    assert communication_elements("os+g+p", 1000, 4) == 2250
