@@ -300,3 +300,60 @@ def test_fp32_accumulation_full_shard(Z):
     print(f"\n1T shard, 4 micro-batches: every element within the bar: {ta}; {tl}", flush=True)
     del P, M, V, A, RA, par, ref, opt
     torch.cuda.empty_cache()
+
+
+def test_reduction_full_shard(Z):
+    """The 1T model's last-rank shard (976M params) with its gradient formed
+    as the reduction of 8 ranks' distinct bf16 slices into the fp32 copy, the
+    copy's norm in the same pass (as bench.py --reduce 8 runs it), then the
+    step on that copy: the oracle reduces the same slices in rank order, takes
+    the norm over the whole fp32 copy, and every element of the copy (within
+    1 fp32 ulp) and of the updated state is compared."""
+    w = W.GPT_1T_LAST_RANK
+    K = 8
+    _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+    begin = w.rank * S
+    real = min(S, max(0, W.real_total(w) - begin))
+    blocks = F.chunk_blocks(begin, S)
+    inv = 1.0 / (K * w.loss_scale)                 # the mean over the ranks, folded into the unscale
+    P, M, V = _f32(S), _f32(S), _f32(S)
+    slices = [torch.empty(S, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+    acc_host = np.empty(S, np.float32)
+
+    def red_task(b):
+        lo, hi = b
+        gs = [W.fill(w, "grad", begin + lo, hi - lo, step=600 + k, threads=1) for k in range(K)]
+        for a, c in F.by_sub(hi - lo):
+            acc_host[lo + a:lo + c], ovf = oracle.grad_reduce([g[a:c] for g in gs], "bf16", inv)
+            assert not ovf
+        return gs, oracle.sqnorm_terms(acc_host[lo:hi], "f32", 1.0)
+
+    terms = []
+    for (lo, hi), (gs, tm) in F.pmap(red_task, blocks):
+        for k in range(K):
+            _put(slices[k], lo, gs[k])
+        terms.append(tm)
+    ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, "f32", 1.0)
+    ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
+    _state_and_reference(w, begin, blocks, acc_host, "f32", ref_sq, _hp(w, w.step, 1.0), (P, M, V), ref)
+    A = _f32(S)
+    par = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                      max_grad_norm=w.max_grad_norm, applied_steps=w.step - 1, device_state=True,
+                      scaler=Z.LossScaler.static(K * w.loss_scale))
+    opt.reduce(A, slices, with_norm=True)
+    opt.step(A, par, norm_done=True)
+    st = opt.read_state()
+    del slices
+    assert st.last_overflow == int(ref_ovf) == 0 and st.applied == w.step
+    check_norm(opt.sqnorm.item(), ref_sq)
+    RA = torch.from_numpy(acc_host).cuda()
+    ta = F.Tally("fp32 gradient copy (1 ulp)")
+    for lo, hi in blocks:
+        F.tally_ulp_f32(ta, A[lo:hi], RA[lo:hi], lo)
+    F.assert_all([ta])
+    tl = _compare(blocks, (P, M, V, par), ref, "reduced ", w.param_dtype)
+    _padding_zero(real, S, (P, M, V, A), par)
+    print(f"\n1T shard, 8 ranks' slices reduced: every element within the bar: {ta}; {tl}", flush=True)
+    del P, M, V, A, RA, par, ref, opt
+    torch.cuda.empty_cache()
