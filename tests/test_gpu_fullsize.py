@@ -357,3 +357,47 @@ def test_reduction_full_shard(Z):
     print(f"\n1T shard, 8 ranks' slices reduced: every element within the bar: {ta}; {tl}", flush=True)
     del P, M, V, A, RA, par, ref, opt
     torch.cuda.empty_cache()
+
+
+def test_offload_full_shard(Z):
+    """The 1T model's last-rank shard (976M params) stepped with its fp32
+    state in pinned host memory (as bench.py --offload runs it: the norm on
+    the device, the AdamW step on host cores, the 16-bit parameters back to
+    the device): every element of the host state and of the device parameter
+    copy against the oracle."""
+    w = W.GPT_1T_LAST_RANK
+    _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
+    begin = w.rank * S
+    real = min(S, max(0, W.real_total(w) - begin))
+    fmt, inv = w.grad_dtype, 1.0 / w.loss_scale
+    blocks = F.chunk_blocks(begin, S)
+    host = [torch.empty(S, dtype=torch.float32, pin_memory=True) for _ in range(3)]
+    G = torch.empty(S, dtype=TDT[fmt], device="cuda")
+    ghost = np.empty(S, np.uint16)
+
+    def grad_task(b):
+        lo, hi = b
+        ghost[lo:hi] = W.fill(w, "grad", begin + lo, hi - lo, step=w.step, threads=1)
+        return oracle.sqnorm_terms(ghost[lo:hi], fmt, inv)
+
+    terms = []
+    for (lo, hi), tm in F.pmap(grad_task, blocks):
+        _put(G, lo, ghost[lo:hi])
+        terms.append(tm)
+    ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, fmt, inv)
+    ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
+    _state_and_reference(w, begin, blocks, ghost, fmt, ref_sq, _hp(w, w.step, inv), host, ref)
+    del ghost
+    par = torch.empty(S, dtype=TDT[w.param_dtype], device="cuda")
+    opt = Z.OffloadShardAdam(*host, grad_dtype=TDT[fmt], param_dtype=TDT[w.param_dtype], lr=w.lr, beta1=w.beta1,
+                             beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_grad_norm=w.max_grad_norm,
+                             scaler=Z.LossScaler.static(w.loss_scale), applied_steps=w.step - 1)
+    assert opt.step(G, par) is False and opt.t == w.step and not ref_ovf
+    check_norm(opt.sqnorm, ref_sq)
+    _padding_zero(real, S, host, par)
+    got = tuple(t.cuda() for t in host) + (par,)          # compared on the device, as the other shards
+    del host, opt
+    tl = _compare(blocks, got, ref, "offloaded ", w.param_dtype)
+    print(f"\n1T shard, CPU offload: every element within the bar: {tl}", flush=True)
+    del got, G, par, ref
+    torch.cuda.empty_cache()
