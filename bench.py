@@ -133,12 +133,13 @@ def _oracle_worker(job):
     return sum(n for _, n in blocks), spent
 
 
-def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, reduce=0):
+def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1 << 22, reduce=0, per_proc=6):
     """The CPU oracle timed on a bounded sample of the same shard, blocks of
     consecutive parameters from its start, one step per block:
       all cores  one process per host core this process may run on (its
-                 affinity set), two blocks of `par_block` each; rate =
-                 sampled params / the busiest process's oracle time;
+                 affinity set), `per_proc` blocks of `par_block` each (about
+                 a second of oracle time per process); rate = sampled params /
+                 the busiest process's oracle time;
       one core   one process, blocks of `block` until `target_s` seconds of
                  oracle time.
     Runs before the GPU is touched (workers are forked)."""
@@ -146,7 +147,7 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1
 
     affinity = len(os.sched_getaffinity(0))
     cores = max(1, affinity)
-    nblk = min(2 * cores, -(-S // par_block))
+    nblk = min(per_proc * cores, -(-S // par_block))
     blocks = [(begin + k * par_block, min(par_block, S - k * par_block)) for k in range(nblk)]
     jobs = [(w, blocks[j::cores], accum, reduce) for j in range(cores) if blocks[j::cores]]
     with multiprocessing.get_context("fork").Pool(len(jobs)) as pool:
@@ -165,6 +166,7 @@ def cpu_baseline(w, begin, S, accum=0, target_s=10.0, block=1 << 24, par_block=1
                       f"({what}exact norm + AdamW, float64 NumPy), {len(jobs)} processes of one thread "
                       f"each, one per host core of the {affinity} this process may run on "
                       f"(os.cpu_count() {os.cpu_count()}); busiest process {par_time:.1f} s of oracle time, "
+                      f"{sum(r[1] for r in res):.1f} s in all, "
                       f"input generation excluded",
             "one_core": {"value": done / spent, "cores": 1,
                          "sample": f"first {done} params in blocks of {block}, one process, {spent:.1f} s of "
