@@ -231,8 +231,6 @@ def zero_shard_grad_accumulate(acc, grad, inv_loss_scale: float, first: bool, ov
              "zero_shard_grad_accumulate")
 
 
-# ---------------------------------------------------------------- host-memory (offload) entry points
-
 MAX_SLICES = 16
 
 
@@ -250,6 +248,8 @@ def zero_shard_grad_reduce(acc, slices, inv_loss_scale: float, overflow=None, gr
                                              float(inv_loss_scale), _typed(overflow, "int32", 1, "overflow"),
                                              _stream(stream)), "zero_shard_grad_reduce")
 
+
+# ---------------------------------------------------------------- host-memory (offload) entry points
 
 def _host_ptr(a) -> Optional[int]:
     """Address of a C-contiguous numpy array or CPU torch tensor."""

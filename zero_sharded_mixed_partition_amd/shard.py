@@ -136,7 +136,7 @@ class ShardAdam:
                                   self.sqnorm if global_sqnorm is None else global_sqnorm,
                                   self.overflow if global_overflow is None else global_overflow)
 
-    def finish(self, global_overflow: Optional[torch.Tensor] = None) -> bool:
+    def finish(self, global_overflow: Optional[torch.Tensor] = None) -> Optional[bool]:
         """Read the overflow flag, update the loss scale and t; returns skip
         (None with device_state: nothing to do on the host)."""
         if self.state is not None:
@@ -152,7 +152,7 @@ class ShardAdam:
 
     def step(self, grad: torch.Tensor, param_out: Optional[torch.Tensor] = None,
              allreduce: Optional[Callable[[torch.Tensor, torch.Tensor], None]] = None,
-             norm_done: bool = False) -> bool:
+             norm_done: bool = False) -> Optional[bool]:
         """One full step.  `allreduce(sqnorm, overflow)`, if given, must turn
         this rank's two scalars into the data-parallel sum / OR in place (on
         one GPU the shard's own values are the global ones).  Returns True if
