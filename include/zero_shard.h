@@ -361,8 +361,11 @@ int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slic
  *   any element is inf/NaN.  grad_dtype ZERO_F16, ZERO_BF16 or ZERO_F32.
  * zero_cpu_shard_adam_step: the fused AdamW update of master/exp_avg/
  *   exp_avg_sq in place and the 16-bit parameter writeback (param_out may be
- *   NULL), with the data-parallel-reduced norm and flag passed by value;
- *   global_overflow != 0 leaves every buffer untouched.
+ *   NULL, any 2-byte alignment), with the data-parallel-reduced norm and flag
+ *   passed by value; global_overflow != 0 leaves every buffer untouched.  The
+ *   parameter copy is written with streaming (non-temporal) stores, so its
+ *   lines are not read first, and the stores are fenced before the call
+ *   returns.
  * nthreads <= 0 uses every hardware thread.  Buffers must not overlap.
  * Errors: ZERO_EINVAL, ZERO_ERANGE.
  * ------------------------------------------------------------------------- */
@@ -377,9 +380,9 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
 
 /* Extra, a measurement aid for the host step: a plain copy of `bytes` (a
  * multiple of 4) from src to dst in host memory, cut into the same chunks and
- * run on the same worker threads, with the same vectorized store style as the
- * host AdamW loop: the achievable rate of one read and one write stream on
- * the host cores.  Synchronous; host pointers, not overlapping; nthreads as
+ * run on the same worker threads, with the same vectorized (ordinary) stores
+ * as the host AdamW loop's fp32 streams: the achievable rate of one read and
+ * one write stream on the host cores.  Synchronous; host pointers, not overlapping; nthreads as
  * above.  Errors: ZERO_EINVAL. */
 int zero_cpu_copy_reference(void* dst, const void* src, int64_t bytes, int32_t nthreads);
 

@@ -10,7 +10,7 @@ import workloads as W
 import zero_sharded_mixed_partition_amd as Z
 from zero_sharded_mixed_partition_amd import _lib as L
 
-from parity import check_norm, compare_step
+from parity import check_norm, check_param, compare_step
 
 CODE = {"f16": L.ZERO_F16, "bf16": L.ZERO_BF16, "f32": L.ZERO_F32}
 SIZES = [1, 3, 7, 8, 2047, 2048, 2049, 65536, 65537, 200_003]
@@ -42,6 +42,31 @@ def test_cpu_step_matches_oracle(n, gfmt, pfmt):
                                param_dtype=CODE[pfmt] if pfmt else None)
     ref = oracle.shard_step(p, m, v, g, gfmt, pfmt, global_sq=ref_sq, global_overflow=False, **hp)
     compare_step((P, M, V, par), ref)
+
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 2049, 65537 + 33])
+@pytest.mark.parametrize("shift", [1, 5, 16])
+def test_param_copy_at_any_alignment(n, shift):
+    """The 16-bit copy is written with streaming stores from its first
+    32-byte boundary on and ordinary stores around it: a copy that starts
+    `shift` elements past an aligned address gets the same bits as an aligned
+    one, and the elements on either side of it stay untouched."""
+    w, p, m, v, g = _inputs("bf16", n, 77 + n)
+    hp = Z.AdamHyper(lr=w.lr, weight_decay=0.05, max_grad_norm=0.01, step=5)
+    sq, _ = Z.zero_cpu_shard_unscale_norm_overflow(g, 1.0, grad_dtype=L.ZERO_BF16)
+    outs = []
+    for off in (0, shift):
+        buf = np.full(n + 64, 0xABCD, np.uint16)
+        base = (-buf.ctypes.data // 2) % 16                 # first 32-byte aligned element of buf
+        par = buf[base + off:base + off + n]
+        Z.zero_cpu_shard_adam_step(p.copy(), m.copy(), v.copy(), g, par, hp, sq, False, grad_dtype=L.ZERO_BF16,
+                                   param_dtype=L.ZERO_BF16)
+        assert (buf[:base + off] == 0xABCD).all() and (buf[base + off + n:] == 0xABCD).all()
+        outs.append(par.copy())
+    assert (outs[0] == outs[1]).all()
+    ref = oracle.shard_step(p, m, v, g, "bf16", "bf16", global_sq=sq, global_overflow=False, lr=w.lr, beta1=0.9,
+                            beta2=0.999, eps=1e-8, weight_decay=0.05, max_grad_norm=0.01, step=5, inv_loss_scale=1.0)
+    check_param("param", outs[1], ref[3], fmt="bf16")
 
 
 def test_thread_count_does_not_change_results():

@@ -24,6 +24,7 @@
 #include <thread>
 #include <vector>
 
+#include <immintrin.h>
 #include <unistd.h>
 
 #include "common.h"
@@ -168,6 +169,27 @@ ZS_CLONES void adam_f32(float* __restrict p, float* __restrict m, float* __restr
         m[i] = mi;
         v[i] = vi;
     }
+}
+
+// dst[0, n) = src[0, n) for the 16-bit parameter copy, with non-temporal
+// (streaming) stores from the first 32-byte boundary of dst on: the host
+// never reads the copy back, so its cache lines need not be fetched before
+// they are written (the write-allocate read, 2 bytes per element).  Ordinary
+// stores cover the unaligned head and the tail.  The caller issues an sfence
+// before the copy is handed on.
+typedef uint16_t u16x16 __attribute__((vector_size(32)));
+ZS_CLONES void store_stream16(uint16_t* __restrict dst, const uint16_t* __restrict src, int n) {
+    int i = 0;
+    while (i < n && (reinterpret_cast<uintptr_t>(dst + i) & 31u) != 0) {
+        dst[i] = src[i];
+        ++i;
+    }
+    for (; i + 16 <= n; i += 16) {
+        u16x16 v;
+        std::memcpy(&v, src + i, sizeof(v));
+        __builtin_nontemporal_store(v, reinterpret_cast<u16x16*>(dst + i));
+    }
+    for (; i < n; ++i) dst[i] = src[i];
 }
 
 // dst = src over n floats, in the same vectorized store style as adam_f32
@@ -370,6 +392,7 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
     const int64_t nchunks = (n + kChunk - 1) / kChunk;
     for_chunks(nchunks, resolve_threads(nthreads, nchunks), [&](int64_t ch) {
         float g[kTile];
+        uint16_t p16[kTile];
         const int64_t lo = ch * kChunk, hi = lo + kChunk < n ? lo + kChunk : n;
         for (int64_t e = lo; e < hi; e += kTile) {
             const int cnt = (int)(hi - e < kTile ? hi - e : kTile);
@@ -377,11 +400,14 @@ int zero_cpu_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, c
             adam_f32(master + e, exp_avg + e, exp_avg_sq + e, g, cnt, gscale, c.beta1, c.omb1, c.beta2, c.omb2,
                      c.step_size, c.rsqrt_bc2, c.eps, c.decay);
             if (param_out != nullptr) {
-                uint16_t* po = static_cast<uint16_t*>(param_out) + e;
-                if (param_dtype == ZERO_F16) encode_f16(master + e, po, cnt);
-                else encode_bf16(master + e, po, cnt);
+                if (param_dtype == ZERO_F16) encode_f16(master + e, p16, cnt);
+                else encode_bf16(master + e, p16, cnt);
+                store_stream16(static_cast<uint16_t*>(param_out) + e, p16, cnt);
             }
         }
+        // the streaming stores are weakly ordered: complete them before this
+        // chunk counts as done (the caller may hand the copy to a DMA engine)
+        _mm_sfence();
     });
     return ZERO_OK;
 }
