@@ -48,6 +48,28 @@ class OffloadShardAdam:
         self._scalars = torch.empty(2, dtype=torch.float64, pin_memory=True)
         self.last_times = {}          # seconds spent in each phase of the last step
 
+    def chunk_bounds(self):
+        """[(lo, hi)] of the pipeline's chunks.  The first and last chunks are
+        small and double up to (and down from) `chunk`: the host starts once
+        the first small chunk has crossed PCIe, and only a small last chunk's
+        parameters cross back after the host has finished.  Bounds are
+        multiples of 1024 elements except where the shard's ragged end falls."""
+        ramp, s = [], max(1024, self.chunk // 8 // 1024 * 1024)
+        while s < self.chunk:
+            ramp.append(s)
+            s *= 2
+        if self.n <= 2 * sum(ramp) + self.chunk:
+            return [(lo, min(self.n, lo + self.chunk)) for lo in range(0, self.n, self.chunk)]
+        sizes = ramp[:]
+        mid = self.n - 2 * sum(ramp)
+        sizes += [self.chunk] * (mid // self.chunk) + ([mid % self.chunk] if mid % self.chunk else [])
+        sizes += ramp[::-1]
+        bounds, lo = [], 0
+        for k in sizes:
+            bounds.append((lo, lo + k))
+            lo += k
+        return bounds
+
     def fetch_grad(self, grad_dev: torch.Tensor) -> None:
         """Whole device gradient shard -> pinned host buffer (waits for the copy)."""
         self.grad_host.copy_(grad_dev, non_blocking=True)
@@ -94,7 +116,7 @@ class OffloadShardAdam:
             self.last_times = {"norm": t1 - t0, "pipeline": 0.0}
             return True
         self.t += 1
-        chunks = [(lo, min(self.n, lo + self.chunk)) for lo in range(0, self.n, self.chunk)]
+        chunks = self.chunk_bounds()
         cur = torch.cuda.current_stream()
         arrived = []
         if self.device_norm:
