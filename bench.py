@@ -421,6 +421,33 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+class StepMarks:
+    """Named timing points of one step on the current stream.  A HIP event is
+    recorded only where work was enqueued since the last recorded one;
+    otherwise the name stands for that event.  Every recorded event costs the
+    GPU a few microseconds (about 4 us each on MI355X: a small shard's step
+    ran 24% longer with five per step than with none), so the timed steps
+    record two, around the update kernel, and each step starts at the
+    previous step's last event when nothing was enqueued in between."""
+
+    def __init__(self, pool, start=None):
+        self._pool, self.ev = pool, {}
+        self._last, self._dirty = start, start is None
+
+    def mark(self, name):
+        if self._dirty:
+            self._last = self._pool.pop()
+            self._last.record()
+            self._dirty = False
+        self.ev[name] = self._last
+
+    def enqueued(self):
+        self._dirty = True
+
+    def ms(self, a, b):
+        return self.ev[a].elapsed_time(self.ev[b])
+
+
 def run_shard(w, args, K, R, steps, warmup):
     """Uploads workload w's shard, runs `warmup` untimed and `steps` timed
     steps (a synchronize on both sides of the timed region), then 10 skipped
@@ -463,55 +490,60 @@ def run_shard(w, args, K, R, steps, warmup):
     FUSED = bool(K or R) and not args.separate_norm
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if args.graph and ev is None:
+    def step(m=None):
+        if args.graph and m is None:
             return opt.step(G, par)
-        if ev is not None:
-            ev[6].record()
+        mark = m.mark if m is not None else (lambda name: None)
+        done = m.enqueued if m is not None else (lambda: None)
+        mark("start")
         if K:
             for k in range(K):
-                if ev is not None and k == K - 1:
-                    ev[3].record()
-                if ev is not None and k == 0 and K > 1:
-                    ev[7].record()
+                if k == K - 1:
+                    mark("copy0")                # the last micro-batch (with the norm when fused)
+                if k == 0 and K > 1:
+                    mark("first0")
                 opt.accumulate(A, G, first=(k == 0), last=FUSED and k == K - 1)
-                if ev is not None and k == 0 and K > 1:
-                    ev[8].record()
-            if ev is not None:
-                ev[4].record()
+                done()
+                if k == 0 and K > 1:
+                    mark("first1")
+            mark("copy1")
         if R:
-            if ev is not None:
-                ev[3].record()
+            mark("copy0")
             opt.reduce(A, slices, with_norm=FUSED)
-            if ev is not None:
-                ev[4].record()
+            done()
+            mark("copy1")
         grad = A if (K or R) else G
-        if ev is not None:
-            ev[0].record()
+        mark("norm0")
         if FUSED:
             pass                               # the copy's norm and flag came with the pass that wrote it
         elif DS:
             opt.norm_decide(grad)              # the decision (coefficients, scaler, counts) in the norm's last kernel
+            done()
         else:
             opt.unscale_norm(grad)
-        if ev is not None:
-            ev[1].record()
+            done()
+        mark("norm1")
         if FUSED and DS:
             opt.decide(grad)                   # one thread: coefficients, scaler, counts
-        if ev is not None:
-            ev[5].record()
+            done()
+        mark("upd0")
         if DS:
             opt.update(grad, par)
         else:
             opt.apply(grad, par)
-        if ev is not None:
-            ev[2].record()
-        return opt.finish()                    # device_state: None, nothing waits
+        done()
+        mark("upd1")
+        r = opt.finish()                       # device_state: None, nothing waits
+        if not DS:
+            done()                             # the host scaler enqueued the flag's copy
+        return r
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(steps)]
+    n_skip = min(10, steps)
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(9 * (2 * steps + n_skip) + 9)]
+    marks = []
     skipped = 0
     wall = []
     skipped0 = opt.read_state().skipped if DS else 0
@@ -519,43 +551,51 @@ def run_shard(w, args, K, R, steps, warmup):
     t0 = time.perf_counter()
     for k in range(steps):
         ts = time.perf_counter()
+        # device state: nothing is enqueued between steps, so a step starts at
+        # the previous one's last event
+        m = StepMarks(pool, marks[-1].ev["upd1"] if (marks and DS) else None)
         if args.graph:
-            evs[k][6].record()
+            m.mark("start")
             r = step(None)
-            evs[k][2].record()
+            m.enqueued()
+            m.mark("upd1")
         else:
-            r = step(evs[k])
+            r = step(m)
+        marks.append(m)
         skipped += bool(r)                                     # host scaler: the step ended with the flag read
         wall.append(time.perf_counter() - ts)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if DS:
         # nothing waited inside the loop: per-step times from the events, start to next start
-        starts = [e[6] for e in evs]
+        starts = [m.ev["start"] for m in marks]
         wall = [starts[k].elapsed_time(starts[k + 1]) * 1e-3 for k in range(steps - 1)]
-        wall.append(starts[-1].elapsed_time(evs[-1][2]) * 1e-3)
+        wall.append(marks[-1].ms("start", "upd1") * 1e-3)
         skipped = opt.read_state().skipped - skipped0
     print(f"# timed {steps} steps", file=sys.stderr, flush=True)
     if args.graph:
         # a replayed graph has no events between its kernels: the per-kernel
         # times come from the same kernels launched one by one, after the
         # timed region
+        marks = []
         for k in range(steps):
-            step(evs[k])
+            m = StepMarks(pool)
+            step(m)
+            marks.append(m)
         torch.cuda.synchronize()
 
     # skipped steps, timed apart: +inf in one gradient element makes the norm
     # pass raise the flag and the update exit without touching the state
-    n_skip = min(10, steps)
     keep = G[S // 2].clone()
     G[S // 2] = float("inf")
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(n_skip)]
+    sev = []
     skipped1 = opt.read_state().skipped if DS else 0
     torch.cuda.synchronize()
     skip_wall = []
     for k in range(n_skip):
         ts = time.perf_counter()
-        r = step(sev[k])
+        sev.append(StepMarks(pool))
+        r = step(sev[-1])
         if DS:
             torch.cuda.synchronize()
         else:
@@ -567,8 +607,8 @@ def run_shard(w, args, K, R, steps, warmup):
     torch.cuda.synchronize()
 
     ms_step = (t1 - t0) * 1e3 / steps
-    norm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    adam_ms = sorted(e[5].elapsed_time(e[2]) for e in evs)
+    norm_ms = sorted(m.ms("norm0", "norm1") for m in marks)
+    adam_ms = sorted(m.ms("upd0", "upd1") for m in marks)
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
     adam_bpp = ADAM_F32_BYTES_PER_PARAM if (K or R) else ADAM_BYTES_PER_PARAM
@@ -584,7 +624,7 @@ def run_shard(w, args, K, R, steps, warmup):
     traffic = measured_traffic(run_key)
     accum_stats = None
     if K:
-        acc_ms = mean([e[3].elapsed_time(e[4]) for e in evs])     # the last (non-first) accumulation
+        acc_ms = mean([m.ms("copy0", "copy1") for m in marks])     # the last (non-first) accumulation
         accum_stats = {"micro_batches": K, "kernel": "grad_sum_norm (with the norm)" if FUSED else "grad_accumulate",
                        "avg_ms": acc_ms,
                        "algorithmic_bytes": ACC_BYTES_PER_PARAM * S if K > 1 else ACC_FIRST_BYTES_PER_PARAM * S,
@@ -593,7 +633,7 @@ def run_shard(w, args, K, R, steps, warmup):
         if K > 1:
             # the first micro-batch (2 B read, 4 B written per element) against
             # the widening copy over the same bytes: G (2 B/param) into A (4 B/param)
-            first_ms = mean([e[7].elapsed_time(e[8]) for e in evs])
+            first_ms = mean([m.ms("first0", "first1") for m in marks])
             first_gbps = ACC_FIRST_BYTES_PER_PARAM * S / (first_ms * 1e-3) / 1e9
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for _ in range(3):
@@ -611,7 +651,7 @@ def run_shard(w, args, K, R, steps, warmup):
                                     "widening_copy_gbps": widen_gbps, "frac_of_widening_copy": first_gbps / widen_gbps}
     reduce_stats = None
     if R:
-        red_ms = mean([e[3].elapsed_time(e[4]) for e in evs])
+        red_ms = mean([m.ms("copy0", "copy1") for m in marks])
         reduce_stats = {"slices": R, "kernel": "grad_sum_norm (with the norm)" if FUSED else "grad_reduce",
                         "avg_ms": red_ms, "algorithmic_bytes": red_bpp * S,
                         "gbps": red_bpp * S / (red_ms * 1e-3) / 1e9,
@@ -636,8 +676,8 @@ def run_shard(w, args, K, R, steps, warmup):
         "norm_pass": ({"fused_into": "grad_sum_norm"} if FUSED else
                       {"avg_ms": mean(norm_ms), "gbps": norm_bpp * S / (mean(norm_ms) * 1e-3) / 1e9}),
         "skipped_step": {"steps": n_skip, "ms_per_step": mean(skip_wall) * 1e3,
-                         "norm_ms": mean([e[0].elapsed_time(e[1]) for e in sev]),
-                         "update_ms": mean([e[5].elapsed_time(e[2]) for e in sev])},
+                         "norm_ms": mean([m.ms("norm0", "norm1") for m in sev]),
+                         "update_ms": mean([m.ms("upd0", "upd1") for m in sev])},
         "accumulate": accum_stats,
         "reduce": reduce_stats,
     }

@@ -34,3 +34,42 @@ def test_code_hash_ignores_comments_only():
     b = "/* header */\nint f(int x) {\n\n    return x + 1;  // a different comment\n}\n"
     c = "int f(int x) {\n    return x + 2;  // one more\n}\n"
     assert bench.code_hash(a) == bench.code_hash(b) != bench.code_hash(c)
+
+
+class _FakeEvent:
+    """Stands in for a timing event: record() stamps the next tick."""
+    clock = 0
+
+    def __init__(self):
+        self.t = None
+
+    def record(self):
+        _FakeEvent.clock += 1
+        self.t = _FakeEvent.clock
+
+    def elapsed_time(self, other):
+        return float(other.t - self.t)
+
+
+def test_step_marks_record_only_after_work():
+    """A mark records a new event only when work was enqueued since the last
+    recorded one; a step can start at the previous step's last event."""
+    import bench
+    pool = [_FakeEvent() for _ in range(8)]
+    a = bench.StepMarks(pool)
+    a.mark("start")
+    a.mark("norm0")                           # nothing enqueued: the same event
+    assert a.ev["start"] is a.ev["norm0"] and len(pool) == 7
+    a.enqueued()
+    a.mark("norm1")
+    a.mark("upd0")
+    assert a.ev["norm1"] is a.ev["upd0"] is not a.ev["norm0"] and len(pool) == 6
+    a.enqueued()
+    a.mark("upd1")
+    assert a.ms("start", "upd1") == 2.0 and a.ms("norm0", "norm1") == 1.0 and a.ms("upd0", "upd1") == 1.0
+    b = bench.StepMarks(pool, a.ev["upd1"])   # the next step starts where this one ended
+    b.mark("start")
+    assert b.ev["start"] is a.ev["upd1"] and len(pool) == 5
+    b.enqueued()
+    b.mark("upd1")
+    assert b.ms("start", "upd1") == 1.0 and len(pool) == 4
