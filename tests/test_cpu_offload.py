@@ -203,3 +203,24 @@ def test_host_copy_reference_rejects_bad_arguments():
     assert lib.zero_cpu_copy_reference(None, p, 4, 0) == Z._L.ZERO_EINVAL
     assert lib.zero_cpu_copy_reference(p, p + 16, 32, 0) == Z._L.ZERO_EINVAL          # overlapping
     assert lib.zero_cpu_copy_reference(p, p + 128, 0, 0) == Z._L.ZERO_OK
+
+
+@pytest.mark.parametrize("n,chunk", [(1, 1 << 25), (5000, 1024), (1_000_003, 1 << 18), (976_077_312, 1 << 25),
+                                     (3 * (1 << 25) + 17, 1 << 25), (1 << 25, 1 << 25), (720_897, 1 << 18)])
+def test_offload_chunks_tile_the_shard(n, chunk):
+    """The offload pipeline's chunks cover [0, n) in order with no gap or
+    overlap; none exceeds `chunk`; on long shards the first and last three
+    ramp by doubling (chunk/8, chunk/4, chunk/2, when those are whole
+    multiples of 1024 elements)."""
+    class Bounds(Z.OffloadShardAdam):
+        def __init__(self, n, chunk):                 # the chunking only: no buffers
+            self.n, self.chunk = n, max(1024, chunk // 1024 * 1024)
+
+    b = Bounds(n, chunk).chunk_bounds()
+    assert b[0][0] == 0 and b[-1][1] == n
+    assert all(lo < hi and hi - lo <= chunk for lo, hi in b)
+    assert all(x[1] == y[0] for x, y in zip(b, b[1:]))
+    sizes = [hi - lo for lo, hi in b]
+    if chunk % 8192 == 0 and n > 2 * (chunk // 8 + chunk // 4 + chunk // 2) + chunk:
+        ramp = [chunk // 8, chunk // 4, chunk // 2]
+        assert sizes[:3] == ramp and sizes[-3:] == ramp[::-1]

@@ -34,7 +34,7 @@ def test_offload_trajectory(Z, wname, device_norm):
                              max_grad_norm=w.max_grad_norm,
                              scaler=(Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0
                                      else Z.LossScaler.static(1.0)), applied_steps=3,
-                             device_norm=device_norm, chunk=1 << 18)      # 4 pipelined chunks
+                             device_norm=device_norm, chunk=1 << 18)      # 9 pipelined chunks, ramped at both ends
     par_dev = torch.zeros(n, dtype=tdt[w.param_dtype], device="cuda")
     state, scaler, t = (p, m, v), oracle.LossScalerState(scale=opt.scaler.scale, backoff=opt.scaler.s.backoff,
                                                           growth=opt.scaler.s.growth,
