@@ -254,7 +254,9 @@ int zero_shard_adam_step(float* master, float* exp_avg, float* exp_avg_sq, const
  * zero_shard_adam_step_coef is zero_shard_adam_step with that block read
  * from device memory d_coef (8-byte aligned) when the kernel runs, so a
  * recorded launch can be replayed with new coefficients; d_global_sqnorm is
- * required.
+ * required.  Every workgroup reads d_coef while others write the shard, so
+ * it must not lie in master, exp_avg, exp_avg_sq or param_out (the caller's
+ * responsibility: unlike the norm and flag, it is not checked).
  *
  * A step graph records, once, on its own stream: the copy of the coefficient
  * block from pinned host memory, the norm pass (as
@@ -447,7 +449,8 @@ int zero_loss_scaler_update(zero_loss_scaler* s, int32_t overflow, int32_t* skip
  *   accumulation and reduction with inv_loss_scale = 1/scale from d_state.
  * In a data-parallel job every rank holds its own copy of the state; since
  * all ranks see the same global overflow flag, the copies stay identical.
- * Calls on one state must be ordered on one stream.
+ * Calls on one state must be ordered on one stream.  The state and d_coef
+ * must not lie in any buffer the same call writes (not checked).
  * Errors: as the host-scaled calls, plus ZERO_EINVAL / ZERO_EALIGN for the
  * state pointer.
  * ------------------------------------------------------------------------- */
