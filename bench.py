@@ -308,7 +308,7 @@ def main():
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on ONE GPU; --gpus {args.gpus} is not supported "
-              "(the data-parallel collectives around the step are not part of this build).", file=sys.stderr)
+              "(the data-parallel collectives around the step are outside this benchmark).", file=sys.stderr)
         sys.exit(2)
 
     import workloads as W
