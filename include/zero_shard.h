@@ -232,6 +232,18 @@ typedef struct {
  * Per element (float32): g = grad * gscale with gscale = float(inv_scale *
  * coef); m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g^2;
  * p = p*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps).
+ * Exactly, with every operation rounded once to float32 (IEEE, nearest
+ * even; fma(a, b, c) = a*b + c with one rounding; sqrt and / correctly
+ * rounded) and the coefficients B1 = float(b1), O1 = float(1 - b1),
+ * B2 = float(b2), O2 = float(1 - b2), SS = float(lr / (1 - b1^t)),
+ * RB = float(1 / sqrt(1 - b2^t)), E = float(eps), D = float(1 - lr*wd)
+ * formed in double (b^t by binary exponentiation: r = 1; while t: if t odd,
+ * r = r*b; b = b*b; t = t/2):
+ *     g = raw * gscale;  m = fma(B1, m, O1*g);  v = fma(B2, v, (O2*g)*g);
+ *     d = fma(sqrt(v), RB, E);  p = fma(p, D, -((SS*m) / d)),
+ * where coef = max_grad_norm / (sqrt(global sum of squares) + 1e-6) in
+ * double, taken as 1 unless it is below 1 (clipping off: coef = 1).  The
+ * results are reproducible bit for bit from this description.
  * Streams 28 bytes per element (2 grad + 3x4 read, 3x4 write + 2 param;
  * 30 with an fp32 gradient).
  * grad must not alias master, exp_avg, exp_avg_sq or param_out, and

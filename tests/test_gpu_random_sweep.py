@@ -9,12 +9,15 @@ of master, moments and gradient, and whether the moments start at zero.
 The step runs three ways: the norm pass with a workspace and the update
 with coefficients from the host; the norm pass without a workspace; and
 the norm pass that forms the coefficients on the device from the step
-state, followed by the update reading them.  All three agree bit for bit,
-and the result is within the bar of the oracle's.
+state, followed by the update reading them.  All three agree bit for bit;
+master and moments equal, bit for bit, the float32 model of the operation
+order the header documents (`f32model`); and the result is within the bar
+of the oracle's.
 """
 import numpy as np
 import pytest
 
+import f32model
 import oracle
 
 from parity import bits_of, check_norm, compare_step, to_device
@@ -40,6 +43,16 @@ def _bits(x: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "f16":
         return x.astype(np.float16).view(np.uint16)
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _values(g: np.ndarray, fmt: str) -> np.ndarray:
+    """Gradient values as float32: 16-bit patterns decoded exactly (IEEE
+    half by numpy, bfloat16 as the upper half of a float32), or the fp32 copy."""
+    if fmt == "f32":
+        return np.asarray(g, np.float32)
+    if fmt == "f16":
+        return g.view(np.float16).astype(np.float32)
+    return (g.astype(np.uint32) << 16).view(np.float32)
 
 
 def _case(i: int):
@@ -113,6 +126,11 @@ def test_random_step(Z, i):
     for a, b, c in ((P, P1, P2), (M, M1, M2), (V, V1, V2)) + (((par, par1, par2),) if pfmt else ()):
         iv = torch.int16 if a.element_size() == 2 else torch.int32
         assert torch.equal(a.view(iv), b.view(iv)) and torch.equal(a.view(iv), c.view(iv)), what
+    # the float32 operation order the header documents, bit for bit, from the GPU's own sum of squares
+    gvals = _values(g, gfmt)
+    model = f32model.adam_update(p, m, v, gvals, sq.item(), **hp)
+    for name, t, x in zip(("master", "exp_avg", "exp_avg_sq"), (P, M, V), model):
+        assert np.array_equal(t.cpu().numpy().view(np.uint32), x.view(np.uint32)), what + name + " != float32 model"
     ref = oracle.shard_step(p, m, v, g, gfmt, pfmt, global_sq=ref_sq, global_overflow=False, **hp)
     got = (P.cpu().numpy(), M.cpu().numpy(), V.cpu().numpy(), bits_of(par) if pfmt else None)
     compare_step(got, ref, what=what, pfmt=pfmt)
