@@ -1,5 +1,8 @@
 """GPU parity at full workload sizes, every element of the shard, in the
-launch configuration the benchmark times.
+launch configuration the benchmark times.  Besides the oracle's bar, every
+element of master, exp_avg and exp_avg_sq of the device steps must equal the
+float32 model of the header's documented operation order (f32model) bit for
+bit.
 
 Inputs are drawn chunk by chunk on the host (a pool of threads, see
 `fullshard`) and copied into HBM.  The oracle computes the exact gradient norm
@@ -14,6 +17,7 @@ import time
 import numpy as np
 import pytest
 
+import f32model
 import oracle
 import workloads as W
 import fullshard as F
@@ -53,21 +57,36 @@ def _hp(w, step, inv):
                 max_grad_norm=w.max_grad_norm, step=step, inv_loss_scale=inv)
 
 
-def _state_and_reference(w, begin, blocks, grad_host, gfmt, ref_sq, hp, dev, ref):
+def _values(g: np.ndarray, fmt: str) -> np.ndarray:
+    """Gradient values as float32: 16-bit patterns decoded exactly, or the fp32 copy."""
+    if fmt == "f32":
+        return np.asarray(g, np.float32)
+    if fmt == "f16":
+        return g.view(np.float16).astype(np.float32)
+    return (g.astype(np.uint32) << 16).view(np.float32)
+
+
+def _state_and_reference(w, begin, blocks, grad_host, gfmt, ref_sq, hp, dev, ref, model=None):
     """Draws master, exp_avg and exp_avg_sq chunk by chunk, runs the oracle's
     step on each chunk (gradient from grad_host, the whole shard's norm
     ref_sq), and moves the inputs into dev = (P, M, V) and the oracle's
-    results into ref = (RP, RM, RV, RPAR)."""
+    results into ref = (RP, RM, RV, RPAR).  With model = three host float32
+    arrays, the float32 model of the documented operation order (f32model)
+    is run on each chunk too, into them."""
     def task(b):
         lo, hi = b
         n = hi - lo
         p, m, v = (W.fill(w, a, begin + lo, n, threads=1) for a in ("master", "exp_avg", "exp_avg_sq"))
         out = (np.empty(n, np.float32), np.empty(n, np.float32), np.empty(n, np.float32), np.empty(n, np.uint16))
         for a, c in F.by_sub(n):
-            r = oracle.shard_step(p[a:c], m[a:c], v[a:c], grad_host[lo + a:lo + c], gfmt, w.param_dtype,
+            g = grad_host[lo + a:lo + c]
+            r = oracle.shard_step(p[a:c], m[a:c], v[a:c], g, gfmt, w.param_dtype,
                                   global_sq=ref_sq, global_overflow=False, **hp)
             for k in range(4):
                 out[k][a:c] = r[k]
+            if model is not None:
+                for dst, x in zip(model, f32model.adam_update(p[a:c], m[a:c], v[a:c], _values(g, gfmt), ref_sq, **hp)):
+                    dst[lo + a:lo + c] = x
         return (p, m, v), out
 
     for (lo, _), (ins, out) in F.pmap(task, blocks):
@@ -97,6 +116,21 @@ def _compare(blocks, got, ref, what, pfmt, strict=True):
     tl = list(tl.values())
     F.assert_all(tl)
     return tl
+
+
+def _check_model(blocks, got, model, gpu_sq, ref_sq, hp):
+    """Every element of the GPU's master, exp_avg and exp_avg_sq equals the
+    float32 model bit for bit.  The model ran with the oracle's sum of
+    squares; the gradient factor it gives must be the one the GPU's own sum
+    gives, so the two ran the same arithmetic."""
+    fac = lambda sq: f32model.gradient_factor(hp["inv_loss_scale"], hp["max_grad_norm"], sq)  # noqa: E731
+    assert fac(gpu_sq) == fac(ref_sq), "gradient factor from the GPU's norm differs from the oracle's"
+    bad = 0
+    for lo, hi in blocks:
+        for t, x in zip(got, model):
+            bad += int((t[lo:hi].cpu().numpy().view(np.uint32) != x[lo:hi].view(np.uint32)).sum())
+    assert bad == 0, f"{bad} elements differ from the float32 model"
+    return bad
 
 
 def _padding_zero(real, S, tensors, par):
@@ -135,7 +169,8 @@ def test_single_step_full_shard(Z, wname):
     ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, fmt, inv)
     hp = _hp(w, w.step, inv)
     ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
-    _state_and_reference(w, begin, blocks, ghost, fmt, ref_sq, hp, (P, M, V), ref)
+    model = tuple(np.empty(S, np.float32) for _ in range(3))
+    _state_and_reference(w, begin, blocks, ghost, fmt, ref_sq, hp, (P, M, V), ref, model)
     del ghost
     t1 = time.perf_counter()
     # the launch configuration bench.py times: step state in device memory, the
@@ -149,8 +184,10 @@ def test_single_step_full_shard(Z, wname):
     assert st.last_overflow == int(ref_ovf) == 0 and st.applied == w.step
     check_norm(opt.sqnorm.item(), ref_sq)
     tl = _compare(blocks, (P, M, V, par), ref, f"{w.name} ", w.param_dtype)
+    _check_model(blocks, (P, M, V), model, opt.sqnorm.item(), ref_sq, hp)
+    del model
     _padding_zero(real, S, (P, M, V), par)
-    print(f"\n{w.name}: S={S} every element within the bar: {tl}; host+upload {t1 - t0:.1f} s, "
+    print(f"\n{w.name}: S={S} every element within the bar and equal to the float32 model: {tl}; host+upload {t1 - t0:.1f} s, "
           f"compare {time.perf_counter() - t1:.1f} s", flush=True)
     del P, M, V, G, par, ref, opt
     torch.cuda.empty_cache()
@@ -164,7 +201,8 @@ def test_trajectory_with_overflow_full_shard(Z):
     against the oracle's loss scaler; norms within the bar after every applied
     step; the two GPU paths bit-identical to each other; and every element of
     both against the oracle's own 20-iteration trajectory, which keeps its
-    float32 state on the host.  Each side rounds its own state every step, so
+    float32 state on the host, and bit for bit against the float32 model's
+    own trajectory.  Each side rounds its own state every step, so
     after 18 applied steps the comparison is held to the bar (1e-5 / 1e-7,
     1 ulp), not to the tighter single-step check of the second moment."""
     w = W.GPT_100B_RANK
@@ -175,11 +213,13 @@ def test_trajectory_with_overflow_full_shard(Z):
     ref_m = np.zeros(S, np.float32)
     ref_v = np.zeros(S, np.float32)
     ref_par = np.empty(S, np.uint16)
+    mod_p, mod_m, mod_v = np.empty(S, np.float32), np.zeros(S, np.float32), np.zeros(S, np.float32)
     Pa, Pb = _f32(S), _f32(S)
 
     def master_task(b):
         lo, hi = b
         ref_p[lo:hi] = W.fill(w, "master", begin + lo, hi - lo, threads=1)
+        mod_p[lo:hi] = ref_p[lo:hi]
 
     for (lo, hi), _ in F.pmap(master_task, blocks):
         _put(Pa, lo, ref_p[lo:hi])
@@ -214,8 +254,12 @@ def test_trajectory_with_overflow_full_shard(Z):
         check_norm(opt_a.sqnorm.item(), ref_sq)
         check_norm(opt_b.sqnorm.item(), ref_sq)
         last = it == w.n_steps
+        hp_t = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t,
+                    inv_loss_scale=inv, max_grad_norm=w.max_grad_norm)
+        fac = lambda sq: f32model.gradient_factor(inv, w.max_grad_norm, sq)  # noqa: E731
+        assert fac(opt_a.sqnorm.item()) == fac(ref_sq), "gradient factor from the GPU's norm differs"
 
-        def step_task(b, t=t, ref_sq=ref_sq, inv=inv, last=last):
+        def step_task(b, t=t, ref_sq=ref_sq, inv=inv, last=last, hp_t=hp_t):
             lo, hi = b
             for a, c in F.by_sub(hi - lo):
                 s = slice(lo + a, lo + c)
@@ -226,6 +270,9 @@ def test_trajectory_with_overflow_full_shard(Z):
                 ref_p[s], ref_m[s], ref_v[s] = r[0], r[1], r[2]
                 if last:
                     ref_par[s] = r[3]
+                # the float32 model carries its own state from step to step
+                mod_p[s], mod_m[s], mod_v[s] = f32model.adam_update(mod_p[s], mod_m[s], mod_v[s],
+                                                                     _values(g[s], "f16"), ref_sq, **hp_t)
 
         for _ in F.pmap(step_task, blocks):
             pass
@@ -237,7 +284,13 @@ def test_trajectory_with_overflow_full_shard(Z):
     ref = tuple(torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
                 for a in (ref_p, ref_m, ref_v, ref_par))
     tl = _compare(blocks, (Pa, Ma, Va, par_a), ref, "after 20 iterations ", "f16", strict=False)
-    print(f"\n100B rank shard, 20 iterations: every element within the bar: {tl}", flush=True)
+    bad = 0
+    for lo, hi in blocks:
+        for t_, x in ((Pa, mod_p), (Ma, mod_m), (Va, mod_v)):
+            bad += int((t_[lo:hi].cpu().numpy().view(np.uint32) != x[lo:hi].view(np.uint32)).sum())
+    assert bad == 0, f"{bad} elements differ from the float32 model's 20-iteration trajectory"
+    print(f"\n100B rank shard, 20 iterations: every element within the bar and equal to the float32 model: {tl}",
+          flush=True)
     del Pa, Pb, Ma, Mb, Va, Vb, G, par_a, par_b, ref, opt_a, opt_b
     torch.cuda.empty_cache()
 
@@ -277,7 +330,9 @@ def test_fp32_accumulation_full_shard(Z):
         terms.append(tm)
     ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, "f32", 1.0)
     ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
-    _state_and_reference(w, begin, blocks, acc_host, "f32", ref_sq, _hp(w, w.step, 1.0), (P, M, V), ref)
+    hp = _hp(w, w.step, 1.0)
+    model = tuple(np.empty(S, np.float32) for _ in range(3))
+    _state_and_reference(w, begin, blocks, acc_host, "f32", ref_sq, hp, (P, M, V), ref, model)
     A = _f32(S)
     par = torch.empty(S, dtype=torch.bfloat16, device="cuda")
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
@@ -296,6 +351,8 @@ def test_fp32_accumulation_full_shard(Z):
         F.tally_ulp_f32(ta, A[lo:hi], RA[lo:hi], lo)
     F.assert_all([ta])
     tl = _compare(blocks, (P, M, V, par), ref, "accumulated ", w.param_dtype)
+    _check_model(blocks, (P, M, V), model, opt.sqnorm.item(), ref_sq, hp)
+    del model
     _padding_zero(real, S, (P, M, V, A), par)
     print(f"\n1T shard, 4 micro-batches: every element within the bar: {ta}; {tl}", flush=True)
     del P, M, V, A, RA, par, ref, opt
@@ -335,7 +392,9 @@ def test_reduction_full_shard(Z):
         terms.append(tm)
     ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, "f32", 1.0)
     ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
-    _state_and_reference(w, begin, blocks, acc_host, "f32", ref_sq, _hp(w, w.step, 1.0), (P, M, V), ref)
+    hp = _hp(w, w.step, 1.0)
+    model = tuple(np.empty(S, np.float32) for _ in range(3))
+    _state_and_reference(w, begin, blocks, acc_host, "f32", ref_sq, hp, (P, M, V), ref, model)
     A = _f32(S)
     par = torch.empty(S, dtype=torch.bfloat16, device="cuda")
     opt = Z.ShardAdam(P, M, V, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
@@ -353,6 +412,8 @@ def test_reduction_full_shard(Z):
         F.tally_ulp_f32(ta, A[lo:hi], RA[lo:hi], lo)
     F.assert_all([ta])
     tl = _compare(blocks, (P, M, V, par), ref, "reduced ", w.param_dtype)
+    _check_model(blocks, (P, M, V), model, opt.sqnorm.item(), ref_sq, hp)
+    del model
     _padding_zero(real, S, (P, M, V, A), par)
     print(f"\n1T shard, 8 ranks' slices reduced: every element within the bar: {ta}; {tl}", flush=True)
     del P, M, V, A, RA, par, ref, opt
