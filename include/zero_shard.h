@@ -367,7 +367,10 @@ int zero_shard_grad_reduce(float* acc, const void* const* slices, int32_t n_slic
  * glossary description, CPU offloading).  All pointers are HOST pointers
  * (pinned or pageable); the calls are synchronous and return when done.
  * They compute what the device entry points compute, from the same per-step
- * coefficients, in float32 with float64 norm partials:
+ * coefficients: the AdamW update in the float32 operation order documented
+ * for zero_shard_adam_step (fused multiply-adds included), so a host step
+ * and a device step from the same state, gradient and global norm agree bit
+ * for bit; the norm with float64 partials:
  *
  * zero_cpu_shard_unscale_norm_overflow: *sqnorm = sum (grad * inv)^2 over
  *   [0, n), summed in float64 per 65536-element chunk and then in chunk

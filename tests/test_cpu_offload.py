@@ -5,6 +5,7 @@ import math
 import numpy as np
 import pytest
 
+import f32model
 import oracle
 import workloads as W
 import zero_sharded_mixed_partition_amd as Z
@@ -224,3 +225,28 @@ def test_offload_chunks_tile_the_shard(n, chunk):
     if chunk % 8192 == 0 and n > 2 * (chunk // 8 + chunk // 4 + chunk // 2) + chunk:
         ramp = [chunk // 8, chunk // 4, chunk // 2]
         assert sizes[:3] == ramp and sizes[-3:] == ramp[::-1]
+
+
+@pytest.mark.parametrize("n", [1, 7, 2049, 65537, 200_003])
+@pytest.mark.parametrize("gfmt", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("clip", [0.0, 0.01])
+def test_cpu_step_equals_the_float32_model(n, gfmt, clip):
+    """The host step follows the float32 operation order the header
+    documents for the device update, fused multiply-adds included: master,
+    m and v equal the model bit for bit (so a host step and a device step
+    from the same state agree)."""
+    w, p, m, v, g = _inputs(gfmt, n, 999 + n)
+    inv = 1.0 if gfmt == "f32" else 1.0 / w.loss_scale
+    sq, _ = Z.zero_cpu_shard_unscale_norm_overflow(g, inv, grad_dtype=CODE[gfmt])
+    hp = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.05, max_grad_norm=clip, step=77,
+              inv_loss_scale=inv)
+    P, M, V = p.copy(), m.copy(), v.copy()
+    Z.zero_cpu_shard_adam_step(P, M, V, g, None, Z.AdamHyper(**hp), sq, False, grad_dtype=CODE[gfmt])
+    if gfmt == "f32":
+        gv = np.asarray(g, np.float32)
+    elif gfmt == "f16":
+        gv = g.view(np.float16).astype(np.float32)
+    else:
+        gv = (g.astype(np.uint32) << 16).view(np.float32)
+    for got, want in zip((P, M, V), f32model.adam_update(p, m, v, gv, sq, **hp)):
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -2,7 +2,7 @@
 launch configuration the benchmark times.  Besides the oracle's bar, every
 element of master, exp_avg and exp_avg_sq of the device steps must equal the
 float32 model of the header's documented operation order (f32model) bit for
-bit.
+bit (the offloaded step's host loop follows the same order).
 
 Inputs are drawn chunk by chunk on the host (a pool of threads, see
 `fullshard`) and copied into HBM.  The oracle computes the exact gradient norm
@@ -425,7 +425,9 @@ def test_offload_full_shard(Z):
     state in pinned host memory (as bench.py --offload runs it: the norm on
     the device, the AdamW step on host cores, the 16-bit parameters back to
     the device): every element of the host state and of the device parameter
-    copy against the oracle."""
+    copy against the oracle, and the host master and moments bit for bit
+    against the float32 model (the host loop uses the device's operation
+    order)."""
     w = W.GPT_1T_LAST_RANK
     _, S, _ = Z.zero_partition_plan(w.shapes, w.n_d, w.align)
     begin = w.rank * S
@@ -447,7 +449,9 @@ def test_offload_full_shard(Z):
         terms.append(tm)
     ref_sq, ref_ovf = oracle.combine_sqnorm_terms(terms, fmt, inv)
     ref = (_f32(S), _f32(S), _f32(S), torch.empty(S, dtype=torch.int16, device="cuda"))
-    _state_and_reference(w, begin, blocks, ghost, fmt, ref_sq, _hp(w, w.step, inv), host, ref)
+    hp = _hp(w, w.step, inv)
+    model = tuple(np.empty(S, np.float32) for _ in range(3))
+    _state_and_reference(w, begin, blocks, ghost, fmt, ref_sq, hp, host, ref, model)
     del ghost
     par = torch.empty(S, dtype=TDT[w.param_dtype], device="cuda")
     opt = Z.OffloadShardAdam(*host, grad_dtype=TDT[fmt], param_dtype=TDT[w.param_dtype], lr=w.lr, beta1=w.beta1,
@@ -455,10 +459,12 @@ def test_offload_full_shard(Z):
                              scaler=Z.LossScaler.static(w.loss_scale), applied_steps=w.step - 1)
     assert opt.step(G, par) is False and opt.t == w.step and not ref_ovf
     check_norm(opt.sqnorm, ref_sq)
+    _check_model(blocks, host, model, opt.sqnorm, ref_sq, hp)      # the host loop rounds as the device does
+    del model
     _padding_zero(real, S, host, par)
     got = tuple(t.cuda() for t in host) + (par,)          # compared on the device, as the other shards
     del host, opt
     tl = _compare(blocks, got, ref, "offloaded ", w.param_dtype)
-    print(f"\n1T shard, CPU offload: every element within the bar: {tl}", flush=True)
+    print(f"\n1T shard, CPU offload: every element within the bar and equal to the float32 model: {tl}", flush=True)
     del got, G, par, ref
     torch.cuda.empty_cache()

@@ -38,8 +38,11 @@ namespace {
 constexpr int64_t kChunk = int64_t(1) << 16;   // elements per work item / norm partial
 constexpr int kTile = 2048;                    // elements converted per inner pass (stack buffers)
 
-// Per-ISA clones of the hot loops (AVX-512, AVX2, baseline), picked at load
-// time by resolvers the dynamic loader runs.  A ThreadSanitizer build compiles
+// Per-ISA clones of the hot loops (AVX-512, AVX2 with FMA, baseline), picked
+// at load time by resolvers the dynamic loader runs.  The AdamW loop uses
+// fused multiply-adds: the two vector clones issue them in hardware; the
+// baseline clone (x86-64 without FMA) calls the C library's fmaf, which
+// rounds the same way, slowly.  A ThreadSanitizer build compiles
 // them once: its runtime is not up yet when the loader runs the resolvers.
 #if defined(__has_feature)
 #if __has_feature(thread_sanitizer)
@@ -52,7 +55,7 @@ constexpr int kTile = 2048;                    // elements converted per inner p
 #ifdef ZS_SINGLE_ISA
 #define ZS_CLONES
 #else
-#define ZS_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#define ZS_CLONES __attribute__((target_clones("avx512f", "arch=haswell", "default")))
 #endif
 
 inline uint32_t f2u(float f) {
@@ -156,16 +159,18 @@ ZS_CLONES int any_nonfinite32(const float* __restrict g, int n) {
 }
 
 // AdamW on n elements in place on p, m, v; g holds the raw gradient values
-// (decoded to float) and gscale the unscale-and-clip factor
+// (decoded to float) and gscale the unscale-and-clip factor.  The same
+// float32 operations in the same order as the device update (fused
+// multiply-adds where it has them), so host and device steps agree bit for bit.
 ZS_CLONES void adam_f32(float* __restrict p, float* __restrict m, float* __restrict v, const float* __restrict g,
                         int n, float gscale, float b1, float omb1, float b2, float omb2, float step_size,
                         float rsqrt_bc2, float eps, float decay) {
     for (int i = 0; i < n; ++i) {
         const float gi = g[i] * gscale;
-        const float mi = b1 * m[i] + omb1 * gi;
-        const float vi = b2 * v[i] + (omb2 * gi) * gi;      // finite wherever v is (g g alone overflows past 2^64)
-        const float denom = std::sqrt(vi) * rsqrt_bc2 + eps;
-        p[i] = p[i] * decay - (step_size * mi) / denom;
+        const float mi = std::fma(b1, m[i], omb1 * gi);
+        const float vi = std::fma(b2, v[i], (omb2 * gi) * gi);   // finite wherever v is (g g alone overflows past 2^64)
+        const float denom = std::fma(std::sqrt(vi), rsqrt_bc2, eps);
+        p[i] = std::fma(p[i], decay, -((step_size * mi) / denom));
         m[i] = mi;
         v[i] = vi;
     }
