@@ -16,7 +16,6 @@ from collections import deque
 import os
 from concurrent.futures import ThreadPoolExecutor
 
-import numpy as np
 
 import workloads as W
 from parity import ABS, REL

@@ -4,7 +4,6 @@ The raw calls hand out and take back memory that the library's kernels
 read and write correctly; a torch memory pool backed by the library's
 allocator serves a shard whose step matches the oracle and, bit for bit,
 the same step on buffers from torch's default allocator."""
-import numpy as np
 import pytest
 
 import oracle

@@ -1,7 +1,6 @@
 """GPU + host: the offloaded shard step (device gradient -> pinned host ->
 host-core AdamW -> 16-bit parameters back to the device) against the oracle,
 over a short trajectory with a skipped step."""
-import numpy as np
 import pytest
 
 import oracle
