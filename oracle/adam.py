@@ -33,6 +33,7 @@ import numpy as np
 
 from .formats import FORMATS, decode16, encode16_rne, is_nonfinite16
 
+
 def _magnitude_counts(bits: np.ndarray, fmt: str) -> np.ndarray:
     """How many elements carry each 16-bit magnitude pattern (sign dropped):
     counts[p] for p in [0, 0x8000)."""
