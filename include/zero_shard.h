@@ -626,10 +626,13 @@ int zero_norm_combine_ranks(const double* slot_sqnorm, const int32_t* slot_overf
  *   only when that fails too.  The stream argument is unused.
  * zero_pool_counts: how many segments zero_pool_alloc has handed out since
  *   the library was loaded, physically contiguous (*contiguous) and fallen
- *   back to ordinary device memory (*fallback), over all devices.  These two
- *   process-wide counters are the library's only state besides the
- *   thread-local error string.  Errors: ZERO_EINVAL (NULL output).
- * These calls and the step graphs are the only ones that allocate.
+ *   back to ordinary device memory (*fallback), over all devices: two
+ *   process-wide counters, the allocator's only state.  Errors: ZERO_EINVAL
+ *   (NULL output).
+ * These calls and the step graphs are the only ones that allocate device or
+ * pinned memory.  (The other state the library keeps is listed at the head
+ * of this header: the host step's worker threads and, per GPU, the fixed
+ * array of the allocation-free norm pass and its looked-up address.)
  * ------------------------------------------------------------------------- */
 int zero_device_alloc_contiguous(void** ptr, size_t bytes);
 int zero_device_free(void* ptr);
