@@ -55,3 +55,32 @@ def test_model_within_the_bar_of_the_oracle(seed):
     for got, ref in ((mp, rp), (mm, rm), (mv, rv)):
         err = np.abs(got.astype(np.float64) - ref)
         assert (err <= np.maximum(1e-5 * np.abs(ref), 1e-7)).all()
+
+
+def test_cancellation_floor_values():
+    """4 float32 ulps of the larger subtracted term; below the bar unless
+    the two terms cancel."""
+    from parity import cancellation_floor
+    f = cancellation_floor(np.array([0.7, 0.02, -0.5], np.float32), np.array([0.005, 0.0199, -0.49]), 0.99)
+    assert f[0] == 4 * np.spacing(np.float32(0.7 * 0.99))          # |p D| = 0.693 > |p D - ref| = 0.688
+    assert f[1] == 4 * np.spacing(np.float32(0.02 * 0.99))
+    rng = np.random.default_rng(3)
+    p = rng.standard_normal(100_000) * rng.choice([0.02, 1.0, 30.0], 100_000)
+    ref = p * 0.999 - rng.standard_normal(100_000) * 1e-3 * np.abs(p)     # no cancellation
+    bar = np.maximum(1e-5 * np.abs(ref), 1e-7)
+    assert (cancellation_floor(p, ref, 0.999) <= bar).all()
+
+
+def test_cancelling_case_passes_only_with_the_floor():
+    """A random-sweep case in the cancellation regime (reading R18): the
+    float32 model, which the GPU equals bit for bit, leaves the plain bar on
+    a few masters and stays within the raised floor."""
+    import test_gpu_random_sweep as T
+    from parity import cancellation_floor, check_f32
+    n, gfmt, pfmt, p, m, v, g, hp = T._case(346)
+    sq, _ = oracle.shard_sqnorm_overflow(g, gfmt, hp["inv_loss_scale"])
+    rp = oracle.shard_step(p, m, v, g, gfmt, None, global_sq=sq, global_overflow=False, **hp)[0]
+    mp = f32model.adam_update(p, m, v, T._values(g, gfmt), sq, **hp)[0]
+    with pytest.raises(AssertionError):
+        check_f32("master", mp, rp)
+    check_f32("master", mp, rp, floor=cancellation_floor(p, rp, 1.0 - hp["lr"] * hp["weight_decay"]))

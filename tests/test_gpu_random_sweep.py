@@ -12,7 +12,9 @@ the norm pass that forms the coefficients on the device from the step
 state, followed by the update reading them.  All three agree bit for bit;
 master and moments equal, bit for bit, the float32 model of the operation
 order the header documents (`f32model`); and the result is within the bar
-of the oracle's.
+of the oracle's, the master's absolute floor raised to 4 float32 ulps of the
+larger of its two terms where they cancel (float32's own rounding, which the
+bit-exact model check shows is all that differs there).
 """
 import numpy as np
 import pytest
@@ -20,13 +22,13 @@ import pytest
 import f32model
 import oracle
 
-from parity import bits_of, check_norm, compare_step, to_device
+from parity import bits_of, cancellation_floor, check_norm, compare_step, to_device
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
-N_CASES = 128
+N_CASES = 1024
 
 
 @pytest.fixture(scope="module")
@@ -133,5 +135,7 @@ def test_random_step(Z, i):
         assert np.array_equal(t.cpu().numpy().view(np.uint32), x.view(np.uint32)), what + name + " != float32 model"
     ref = oracle.shard_step(p, m, v, g, gfmt, pfmt, global_sq=ref_sq, global_overflow=False, **hp)
     got = (P.cpu().numpy(), M.cpu().numpy(), V.cpu().numpy(), bits_of(par) if pfmt else None)
-    compare_step(got, ref, what=what, pfmt=pfmt)
+    # the master's floor raised where its two terms cancel (reading R18: float32 rounding of terms near 1)
+    floor = cancellation_floor(p, ref[0], 1.0 - hp["lr"] * hp["weight_decay"])
+    compare_step(got, ref, what=what, pfmt=pfmt, master_floor=floor)
     assert state.read().applied == hp["step"]
