@@ -57,3 +57,47 @@ def test_offload_trajectory(Z, wname, device_norm):
             compare_step((opt.master.numpy(), opt.exp_avg.numpy(), opt.exp_avg_sq.numpy(), bits_of(par_dev)),
                          out, what=f"it{it} ")
         assert opt.t == t and opt.scaler.scale == scaler.scale
+
+
+@pytest.mark.parametrize("wname", ["gpt100b", "gpt1t"])
+def test_device_and_host_steps_interchange(Z, wname):
+    """A shard stepped 3 times on the device, then handed to the offloaded
+    optimizer (state copied to pinned host memory) for 3 more steps, one of
+    them skipped, ends bit-identical to 6 steps on the device: the host loop
+    rounds exactly as the kernel does and both take the norm from the same
+    device pass."""
+    w = W.get(wname)
+    n = 300_007
+    p, m, v, _ = W.shard_inputs(w, 77, n)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    kw = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              max_grad_norm=w.max_grad_norm)
+    mk_scaler = lambda: Z.LossScaler(scale=w.loss_scale) if w.loss_scale != 1.0 else Z.LossScaler.static(1.0)  # noqa: E731
+    grads = []
+    for it in range(6):
+        g = W.fill(w, "grad", 77, n, step=60 + it, loss_scale=w.loss_scale / (2 if it >= 4 else 1))
+        if it == 3:
+            g[n // 3] = W.POS_INF_BITS[w.grad_dtype]          # skipped (scale halves when it is dynamic)
+        grads.append(to_device(g, w.grad_dtype))
+    # all six on the device (host loss scaler, as the offloaded optimizer keeps it)
+    dev = [to_device(a) for a in (p, m, v)]
+    ref_par = torch.empty(n, dtype=tdt[w.param_dtype], device="cuda")
+    opt = Z.ShardAdam(*dev, scaler=mk_scaler(), applied_steps=10, **kw)
+    for g in grads:
+        opt.step(g, ref_par)
+    # three on the device, then three offloaded
+    dev2 = [to_device(a) for a in (p, m, v)]
+    par = torch.empty(n, dtype=tdt[w.param_dtype], device="cuda")
+    opt2 = Z.ShardAdam(*dev2, scaler=mk_scaler(), applied_steps=10, **kw)
+    for g in grads[:3]:
+        opt2.step(g, par)
+    torch.cuda.synchronize()
+    host = [t.cpu().pin_memory() for t in dev2]
+    off = Z.OffloadShardAdam(*host, grad_dtype=tdt[w.grad_dtype], param_dtype=tdt[w.param_dtype], scaler=opt2.scaler,
+                             applied_steps=opt2.t, chunk=1 << 16, **kw)
+    skips = [off.step(g, par) for g in grads[3:]]
+    torch.cuda.synchronize()
+    assert skips == [True, False, False] and off.t == opt.t == 15 and off.scaler.scale == opt.scaler.scale
+    for a, b in zip(host, (opt.master, opt.exp_avg, opt.exp_avg_sq)):
+        assert torch.equal(a.view(torch.int32), b.cpu().view(torch.int32))
+    assert torch.equal(par.view(torch.int16), ref_par.view(torch.int16))
