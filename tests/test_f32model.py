@@ -72,9 +72,9 @@ def test_cancellation_floor_values():
 
 
 def test_cancelling_case_passes_only_with_the_floor():
-    """A random-sweep case in the cancellation regime (reading R18): the
-    float32 model, which the GPU equals bit for bit, leaves the plain bar on
-    a few masters and stays within the raised floor."""
+    """A random-sweep case where the update's two terms (near 0.7 each)
+    cancel: the float32 model, which the GPU equals bit for bit, leaves the
+    plain bar on a few masters and stays within the raised floor."""
     import test_gpu_random_sweep as T
     from parity import cancellation_floor, check_f32
     n, gfmt, pfmt, p, m, v, g, hp = T._case(346)

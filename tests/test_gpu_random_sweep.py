@@ -135,7 +135,7 @@ def test_random_step(Z, i):
         assert np.array_equal(t.cpu().numpy().view(np.uint32), x.view(np.uint32)), what + name + " != float32 model"
     ref = oracle.shard_step(p, m, v, g, gfmt, pfmt, global_sq=ref_sq, global_overflow=False, **hp)
     got = (P.cpu().numpy(), M.cpu().numpy(), V.cpu().numpy(), bits_of(par) if pfmt else None)
-    # the master's floor raised where its two terms cancel (reading R18: float32 rounding of terms near 1)
+    # the master's floor raised where its two terms cancel: float32 rounds terms near 1 to a few 1e-8
     floor = cancellation_floor(p, ref[0], 1.0 - hp["lr"] * hp["weight_decay"])
     compare_step(got, ref, what=what, pfmt=pfmt, master_floor=floor)
     assert state.read().applied == hp["step"]
